@@ -1,0 +1,254 @@
+"""Plain float64 CPU oracle of the MSA routed-layer hot path (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
+leg may use this module.  It shares no code with the HIP path.
+
+Sources (the pages this follows):
+
+* [Design]   MSA README (github.com/EverMind-AI/MSA), section "Overall Design":
+  document latent states K, V and the router key K_r are compressed by taking
+  the mean over fixed-size chunks; a router scores each document by cosine
+  similarity, averaged over heads and then maximised over query tokens; the
+  top-k documents are selected and their compressed K/V are concatenated with
+  the query's own local K/V for attention.
+* [Pipeline] Same page, section "Inference Pipeline": stage 1 caches the
+  chunk-pooled (K, V, K_r) offline; stage 2 projects the query to Q_r, matches
+  it against the pooled K_r, picks the top-k and loads only the selected pooled
+  K/V next to the local context; stage 3 generates over that sparse context.
+* [Card]     william-0g/MSA-Qwen3.5 model card, opening paragraph and
+  "Architecture summary": a per-layer router retrieves the top-k documents
+  from the chunk-pooled bank by cosine routing; in the full (softmax) layers
+  the top-k chunks' K/V are concatenated with the local KV inside sparse
+  attention.
+* [Blog]     moses-y.github.io "MSA" code walk, section "What This Does":
+  restates chunk-mean pooling, cosine routing, top-k and concatenation.
+
+Shapes (row-major, as in the C ABI):
+    raw document tensors   x      [N_doc, L_doc, H, d]
+    pooled bank            xbar   [N_doc * C, H, d]     C = L_doc / chunk
+    router query           q_r    [B, T, H_kv, d_r]
+    doc scores                    [B, N_doc]
+    top-k ids / scores            [B, k]
+    gathered memory        k_sel  [B, k * C, H_kv, d]
+    query                  q      [B, T, H_q, d]
+    local KV               k_loc  [B, L_loc, H_kv, d]
+    output                 o      [B, T, H_q, d]
+    log-sum-exp            lse    [B, H_q, T]
+"""
+
+import numpy as np
+
+from .bf16 import round_bf16, round_f32
+
+EPS = 1e-12
+
+
+# ---------------------------------------------------------------------------
+# S1: chunk-mean pooling
+# ---------------------------------------------------------------------------
+
+def pool_chunks_mean(x, chunk):
+    """Exact chunk mean of each document's rows  ([Design]; [Pipeline] stage 1).
+
+    ``x``: float64 [N_doc, L_doc, H, d].  Returns float64 [N_doc * C, H, d]
+    where row ``n*C + j`` is (1/chunk) * sum_{i<chunk} x[n, j*chunk + i].
+
+    Reading: the pages give no chunk size and never exercise a partial last
+    chunk; L_doc must be a multiple of ``chunk``.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n_doc, l_doc, h, d = x.shape
+    if l_doc % chunk != 0:
+        raise ValueError("document length must be a multiple of the chunk size")
+    c = l_doc // chunk
+    out = np.empty((n_doc, c, h, d), dtype=np.float64)
+    for j in range(c):
+        rows = x[:, j * chunk:(j + 1) * chunk]          # [N_doc, chunk, H, d]
+        out[:, j] = rows.sum(axis=1) / chunk
+    return out.reshape(n_doc * c, h, d)
+
+
+def pool_chunks_stored(x, chunk, dtype):
+    """Chunk mean rounded to the storage dtype ("bf16" or "f32"), as float64.
+
+    Reading: the pooled bank is stored in the dtype of the raw tensors.
+    """
+    m = pool_chunks_mean(x, chunk)
+    if dtype == "bf16":
+        return round_bf16(m)
+    if dtype == "f32":
+        return round_f32(m)
+    raise ValueError(dtype)
+
+
+def chunk_norms(xbar_stored):
+    """Euclidean norm of each stored pooled row, per (chunk, head): [N_ch, H].
+
+    Reading: the norm is taken of the *stored* (rounded) pooled row, because
+    routing consumes the stored rows.
+    """
+    x = np.asarray(xbar_stored, dtype=np.float64)
+    return np.sqrt((x * x).sum(axis=-1))
+
+
+# ---------------------------------------------------------------------------
+# S2: cosine routing
+# ---------------------------------------------------------------------------
+
+def route_scores(q_r, kbar_r, chunks_per_doc, eps=EPS, doc_block=None):
+    """Document scores by cosine routing  ([Design]; [Card] opening; [Pipeline] stage 2).
+
+    For sequence b, token t, pooled chunk n and head h:
+        cos[b,t,n,h] = <q_r[b,t,h], kbar_r[n,h]> / (max(|q_r[b,t,h]|, eps) * max(|kbar_r[n,h]|, eps))
+    then the mean over heads,
+        s[b,t,n] = (1/H) * sum_h cos[b,t,n,h]
+    then the maximum over the query tokens and over the chunks of each document,
+        score[b,doc] = max_{t < T, j < C} s[b, t, doc*C + j].
+
+    Readings: the head mean is taken of per-head cosines (the similarity is
+    pooled, not the vectors); the chunk-to-document reduction is a max; the
+    router has one head per KV head; every query token of the sequence takes
+    part (no causal restriction); ``eps`` only matters for all-zero rows.
+
+    ``doc_block`` optionally evaluates the documents in independent groups to
+    bound memory; each document's score depends only on its own chunks, so
+    the result is identical.
+    """
+    q = np.asarray(q_r, dtype=np.float64)
+    k = np.asarray(kbar_r, dtype=np.float64)
+    b_, t_, h_, d_ = q.shape
+    n_ch = k.shape[0]
+    if k.shape[1:] != (h_, d_):
+        raise ValueError("router query and pooled keys disagree on heads/dim")
+    if n_ch % chunks_per_doc != 0:
+        raise ValueError("chunk count must be a multiple of chunks per document")
+    n_doc = n_ch // chunks_per_doc
+    qn = np.maximum(np.sqrt((q * q).sum(axis=-1)), eps)     # [B, T, H]
+    kn = np.maximum(np.sqrt((k * k).sum(axis=-1)), eps)     # [N_ch, H]
+    if doc_block is None:
+        doc_block = n_doc
+    out = np.empty((b_, n_doc), dtype=np.float64)
+    for d0 in range(0, n_doc, doc_block):
+        d1 = min(n_doc, d0 + doc_block)
+        c0, c1 = d0 * chunks_per_doc, d1 * chunks_per_doc
+        s = np.zeros((b_, t_, c1 - c0), dtype=np.float64)
+        for h in range(h_):
+            dots = q[:, :, h, :] @ k[c0:c1, h, :].T                 # [B, T, n]
+            s += dots / (qn[:, :, h, None] * kn[None, None, c0:c1, h])
+        s /= h_
+        per_chunk = s.max(axis=1)                                    # max over tokens
+        out[:, d0:d1] = per_chunk.reshape(b_, d1 - d0, chunks_per_doc).max(axis=2)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# S3: top-k document selection
+# ---------------------------------------------------------------------------
+
+def topk_docs(scores, k):
+    """The k best documents per sequence  ([Design]; [Pipeline] stage 2).
+
+    Order: score descending; equal scores go to the lower document id.  Returns
+    (ids int64 [B, k], values float64 [B, k]).  Reading: the pages leave the
+    tie rule and output order open; this total order makes the answer unique.
+    """
+    s = np.asarray(scores, dtype=np.float64)
+    b_, n = s.shape
+    if not 1 <= k <= n:
+        raise ValueError("k must lie in [1, N_doc]")
+    ids = np.empty((b_, k), dtype=np.int64)
+    vals = np.empty((b_, k), dtype=np.float64)
+    doc = np.arange(n)
+    for b in range(b_):
+        # lexsort sorts by the last key first: score descending, then id ascending.
+        order = np.lexsort((doc, -s[b]))
+        ids[b] = order[:k]
+        vals[b] = s[b, order[:k]]
+    return ids, vals
+
+
+# ---------------------------------------------------------------------------
+# S4: gather of the selected documents' pooled K/V
+# ---------------------------------------------------------------------------
+
+def gather_kv(kbar, vbar, ids, chunks_per_doc):
+    """Selected documents' pooled K/V, in rank order  ([Pipeline] stage 2).
+
+    k_sel[b, i*C + j] = kbar[ids[b, i]*C + j] and likewise for V.  Reading: the
+    memory rows follow the rank order of the top-k list (softmax does not
+    depend on the order of keys).  Ids outside [0, N_doc) are an error.
+    """
+    kb = np.asarray(kbar)
+    vb = np.asarray(vbar)
+    ids = np.asarray(ids)
+    n_doc = kb.shape[0] // chunks_per_doc
+    if ids.min() < 0 or ids.max() >= n_doc:
+        raise IndexError("document id out of range")
+    b_, k = ids.shape
+    rows = (ids[:, :, None] * chunks_per_doc + np.arange(chunks_per_doc)[None, None, :]).reshape(b_, k * chunks_per_doc)
+    return kb[rows], vb[rows]
+
+
+# ---------------------------------------------------------------------------
+# S5/S6: GQA softmax attention over [selected memory ; local causal KV]
+# ---------------------------------------------------------------------------
+
+def sparse_attention_rows(q_row, keys, values, scale):
+    """Softmax attention of one query row over the given visible keys.
+
+    Returns (o [d], lse).  lse = m + log(sum exp(l - m)), with l = scale*q.k
+    and m = max l.
+    """
+    logits = scale * (keys @ q_row)
+    m = logits.max()
+    p = np.exp(logits - m)
+    l_sum = p.sum()
+    return (p @ values) / l_sum, m + np.log(l_sum)
+
+
+def sparse_attention(q, k_sel, v_sel, k_loc, v_loc, scale=None):
+    """Sparse GQA attention of the MSA layer  ([Card] "Architecture summary";
+    [Design]; [Pipeline] stage 3).
+
+    For sequence b, query token t < T and query head h, with KV head
+    g = h // (H_q / H_kv), the keys are the M gathered memory rows followed by
+    the local rows 0 .. L_loc - T + t (bottom-right causal alignment: the last
+    query token sees every local row), and
+
+        o[b,t,h] = softmax(scale * q[b,t,h] . keys^T) . values.
+
+    Readings: scale defaults to 1/sqrt(d); memory rows are visible to every
+    query token; query heads map to KV heads in contiguous groups; no dropout,
+    window, sink or soft-cap.  For decode (T = 1) the local rows include the
+    new token's own key.
+
+    Returns (o float64 [B, T, H_q, d], lse float64 [B, H_q, T]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    ks = np.asarray(k_sel, dtype=np.float64)
+    vs = np.asarray(v_sel, dtype=np.float64)
+    kl = np.asarray(k_loc, dtype=np.float64)
+    vl = np.asarray(v_loc, dtype=np.float64)
+    b_, t_, hq, d = q.shape
+    m_len = ks.shape[1]
+    l_len = kl.shape[1]
+    hkv = ks.shape[2]
+    if hq % hkv != 0:
+        raise ValueError("query heads must be a multiple of KV heads")
+    if l_len < t_:
+        raise ValueError("local KV must hold at least the query tokens")
+    group = hq // hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    o = np.empty((b_, t_, hq, d), dtype=np.float64)
+    lse = np.empty((b_, hq, t_), dtype=np.float64)
+    for b in range(b_):
+        for h in range(hq):
+            g = h // group
+            keys = np.concatenate([ks[b, :, g], kl[b, :, g]], axis=0)    # [M + L_loc, d]
+            vals = np.concatenate([vs[b, :, g], vl[b, :, g]], axis=0)
+            for t in range(t_):
+                visible = m_len + (l_len - t_ + t + 1)
+                o[b, t, h], lse[b, h, t] = sparse_attention_rows(
+                    q[b, t, h], keys[:visible], vals[:visible], scale)
+    return o, lse
