@@ -1,0 +1,188 @@
+/*
+ * msa.h -- C ABI of libmsa, the MI355X (gfx950) hot path of Memory Sparse
+ * Attention (MSA) for one routed layer.
+ *
+ * The method (MSA README, github.com/EverMind-AI/MSA, "Overall Design" and
+ * "Inference Pipeline"; william-0g/MSA-Qwen3.5 model card, opening paragraph
+ * and "Architecture summary"):
+ *   1. document K, V and router keys K_r are mean-pooled over fixed-size
+ *      chunks into a memory bank (K-bar, V-bar, K_r-bar);
+ *   2. each document is scored by the cosine similarity between the query's
+ *      router projection Q_r and K_r-bar, averaged over heads and maximised
+ *      over query tokens (and over the document's chunks);
+ *   3. the top-k documents are selected;
+ *   4. only their pooled K/V are loaded and placed before the local K/V;
+ *   5. GQA softmax attention runs over that sparse context.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are dense, row-major, in the layouts stated per call.  Pointers
+ *   are device pointers unless stated otherwise, 16-byte aligned.
+ * - The caller owns every buffer.  No entry point allocates device memory;
+ *   scratch space comes from the caller's workspace (`ws`, `ws_bytes`),
+ *   sized by the matching *_workspace call.  (The host-tier gather keeps one
+ *   small library-owned device flag word and side stream per device, created
+ *   on first use and kept until the process ends.)
+ * - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *   All work is enqueued on it, asynchronously; a call returns before the
+ *   GPU has finished unless stated otherwise.
+ * - Argument errors are detected on the host before anything is enqueued and
+ *   returned as MSA_ERR_INVALID (bad value) or MSA_ERR_UNSUPPORTED (valid
+ *   but not implemented).  A failed launch returns MSA_ERR_HIP.  Faults of
+ *   enqueued work surface at the caller's next synchronisation, as in HIP.
+ *   msa_last_error() then returns a description (thread-local).
+ * - No C++ exception crosses this boundary.  Calls are thread-safe; calls on
+ *   one stream execute in order.
+ * - dtype MSA_BF16 stores bfloat16 bit patterns (uint16); MSA_F32 stores
+ *   IEEE float32.  Arithmetic is float32 in either case; rounding to the
+ *   storage dtype is round-to-nearest-even.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum msa_status {
+  MSA_OK = 0,
+  MSA_ERR_INVALID = 1,
+  MSA_ERR_UNSUPPORTED = 2,
+  MSA_ERR_HIP = 3
+} msa_status;
+
+typedef enum msa_dtype { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
+
+/* Gather flags (msa_gather_kv). */
+#define MSA_GATHER_CHECKED 1     /* synchronise and report out-of-range ids as MSA_ERR_INVALID */
+#define MSA_GATHER_HOST_MEMCPY 2 /* host tier: per-document hipMemcpyAsync on a side stream     */
+
+/* Version of this ABI (bumped on any incompatible change). */
+int msa_abi_version(void);
+
+/* Text describing the last non-OK status returned on the calling thread. */
+const char* msa_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * S1  Chunk-mean pooling (MSA README "Overall Design"; "Inference Pipeline",
+ *     stage 1: the offline encoding caches chunk-pooled K, V and K_r).
+ *
+ *   xbar[n*C + j, h, :] = (1/chunk) * sum_{i<chunk} x[n, j*chunk + i, h, :]
+ *
+ * x          [n_docs, doc_len, heads, dim]   input rows (dtype dt)
+ * xbar       [n_docs*C, heads, dim]          output, C = doc_len/chunk (dtype dt)
+ * xbar_norm  [n_docs*C, heads] float32, or NULL: Euclidean norm of each
+ *            *stored* (rounded) pooled row; the routing step consumes it.
+ * Requires doc_len % chunk == 0; heads*dim*sizeof(dt) % 16 == 0; when
+ * xbar_norm is given, dim*sizeof(dt) must be a power of two in [16, 1024].
+ * ---------------------------------------------------------------------- */
+msa_status msa_pool_chunks(const void* x, void* xbar, float* xbar_norm, int64_t n_docs,
+                           int32_t doc_len, int32_t chunk, int32_t heads, int32_t dim,
+                           msa_dtype dt, void* stream);
+
+/* ------------------------------------------------------------------------
+ * S2  Cosine routing scores (MSA README "Overall Design": cosine similarity
+ *     averaged over heads, then maximised over query tokens; model card
+ *     opening paragraph: per-layer router over the chunk-pooled bank).
+ *
+ *   cos[b,t,n,h] = <q_r[b,t,h], kbar_r[n,h]> / (max(|q_r[b,t,h]|,1e-12) * max(kbar_r_norm[n,h],1e-12))
+ *   doc_scores[b, doc] = max_{t<q_len, j<C} (1/heads) * sum_h cos[b, t, doc*C + j, h]
+ *
+ * q_r          [batch, q_len, heads, dim]       router queries (dtype dt)
+ * kbar_r       [n_docs*C, heads, dim]            pooled router keys (dtype dt)
+ * kbar_r_norm  [n_docs*C, heads] float32         their norms (from msa_pool_chunks)
+ * doc_scores   [batch, n_docs] float32           output
+ * ws           msa_route_scores_workspace() bytes of device scratch (may be 0)
+ * Products of bf16 values are exact in float32; per-head dot products are
+ * scaled by the float32 inverse norms (normalised vectors are never rounded).
+ * ---------------------------------------------------------------------- */
+msa_status msa_route_scores_workspace(int32_t batch, int32_t q_len, int32_t heads, int32_t dim,
+                                      int64_t n_docs, int32_t chunks_per_doc, msa_dtype dt,
+                                      size_t* bytes);
+msa_status msa_route_scores(const void* q_r, const void* kbar_r, const float* kbar_r_norm,
+                            int32_t batch, int32_t q_len, int32_t heads, int32_t dim,
+                            int64_t n_docs, int32_t chunks_per_doc, msa_dtype dt,
+                            float* doc_scores, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * S3  Top-k documents (MSA README "Overall Design" and "Inference Pipeline",
+ *     stage 2: pick the top-k documents by routing score).
+ *
+ * The k largest scores of each row, in descending order; equal scores are
+ * ordered by ascending document id (a total order: the result is unique).
+ * -0.0 compares equal to +0.0.  NaN scores are outside the contract.
+ *
+ * doc_scores   [batch, n_docs] float32
+ * topk_ids     [batch, k] int32 output
+ * topk_scores  [batch, k] float32 output, or NULL
+ * Requires 1 <= k <= min(n_docs, 1024), n_docs < 2^31.
+ * ---------------------------------------------------------------------- */
+msa_status msa_topk_docs_workspace(int32_t batch, int64_t n_docs, int32_t k, size_t* bytes);
+msa_status msa_topk_docs(const float* doc_scores, int32_t batch, int64_t n_docs, int32_t k,
+                         int32_t* topk_ids, float* topk_scores, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* ------------------------------------------------------------------------
+ * S4  Gather of the selected documents' pooled K/V ("Inference Pipeline",
+ *     stage 2: load only the selected pooled K/V; the content tier may live
+ *     in host DRAM and be fetched when selected).
+ *
+ *   k_sel[b, i*C + j] = kbar[topk_ids[b,i]*C + j]   (and v_sel from vbar)
+ *
+ * kbar, vbar   [n_docs*C, heads_kv, dim] (dtype dt).  With src_on_host = 0
+ *              they are device pointers; with src_on_host = 1 they point to
+ *              pinned host memory (hipHostMalloc / torch pin_memory), which
+ *              the GPU reads directly over the host link (no host round
+ *              trip), or, with MSA_GATHER_HOST_MEMCPY, which is copied per
+ *              selected document with hipMemcpyAsync on a library side stream
+ *              after the ids are read back (the caller's stream then waits on
+ *              that copy; the call blocks until the ids are on the host).
+ * topk_ids     [batch, k] int32 device pointer
+ * k_sel, v_sel [batch, k*C, heads_kv, dim] device outputs
+ * flags        0 or MSA_GATHER_CHECKED | MSA_GATHER_HOST_MEMCPY.
+ * Ids outside [0, n_docs) never cause an out-of-bounds read: their rows are
+ * written as zeros.  With MSA_GATHER_CHECKED the call synchronises `stream`
+ * and returns MSA_ERR_INVALID if any id was out of range.
+ * ---------------------------------------------------------------------- */
+msa_status msa_gather_kv(const void* kbar, const void* vbar, int32_t src_on_host,
+                         const int32_t* topk_ids, int32_t batch, int32_t k, int64_t n_docs,
+                         int32_t chunks_per_doc, int32_t heads_kv, int32_t dim, msa_dtype dt,
+                         void* k_sel, void* v_sel, int32_t flags, void* stream);
+
+/* ------------------------------------------------------------------------
+ * S5/S6  Sparse GQA attention (model card "Architecture summary": in the
+ *     softmax layers the top-k chunks' K/V are concatenated with the local
+ *     KV; README "Inference Pipeline", stage 3: generate over that context).
+ *
+ * For sequence b, query token t, query head h, KV head g = h / (heads_q/heads_kv):
+ *   keys  = [k_sel[b, 0..mem_len-1, g] ; k_loc[b, 0 .. loc_len-q_len+t, g]]
+ *   o[b,t,h] = softmax(scale * q[b,t,h] . keys^T) . values
+ * (bottom-right causal alignment: the last query token sees all local rows;
+ * memory rows are visible to every token).  lse[b,h,t] = log-sum-exp of the
+ * scaled logits (natural log), for combining partial attentions.
+ *
+ * q            [batch, q_len, heads_q, dim]
+ * k_sel, v_sel [batch, mem_len, heads_kv, dim]  (may be NULL iff mem_len == 0)
+ * k_loc, v_loc [batch, loc_len, heads_kv, dim]  (loc_len >= q_len >= 1)
+ * out          [batch, q_len, heads_q, dim] output (dtype dt)
+ * lse          [batch, heads_q, q_len] float32 output, or NULL
+ * ws           msa_sparse_attn_workspace() bytes (split-KV partials for decode)
+ * Requires heads_q % heads_kv == 0.  scale is typically 1/sqrt(dim).
+ * ---------------------------------------------------------------------- */
+msa_status msa_sparse_attn_workspace(int32_t batch, int32_t q_len, int32_t heads_q,
+                                     int32_t heads_kv, int32_t dim, int32_t mem_len,
+                                     int32_t loc_len, msa_dtype dt, size_t* bytes);
+msa_status msa_sparse_attn(const void* q, const void* k_sel, const void* v_sel, int32_t mem_len,
+                           const void* k_loc, const void* v_loc, int32_t loc_len, int32_t batch,
+                           int32_t q_len, int32_t heads_q, int32_t heads_kv, int32_t dim,
+                           float scale, msa_dtype dt, void* out, float* lse, void* ws,
+                           size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

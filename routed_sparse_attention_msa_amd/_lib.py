@@ -1,0 +1,297 @@
+"""ctypes binding of libmsa (include/msa.h).
+
+Argument marshalling only: each function checks device, dtype, shape and
+contiguity of the torch tensors it is given, allocates missing outputs and
+workspace with torch, and calls the C entry point of the same name on the
+current HIP stream.  Every step of the computation runs in the library's HIP
+kernels; there is no CPU path, and a missing library is an ImportError.
+"""
+
+import ctypes
+import math
+import os
+from ctypes import POINTER, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
+
+MSA_OK, MSA_ERR_INVALID, MSA_ERR_UNSUPPORTED, MSA_ERR_HIP = 0, 1, 2, 3
+MSA_F32, MSA_BF16 = 0, 1
+MSA_GATHER_CHECKED = 1
+MSA_GATHER_HOST_MEMCPY = 2
+
+# Every entry point declared in include/msa.h: name -> (restype, argtypes).
+_STATUS = c_int
+SIGNATURES = {
+    "msa_abi_version": (c_int, []),
+    "msa_last_error": (ctypes.c_char_p, []),
+    "msa_pool_chunks": (_STATUS, [c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_int32, c_int32,
+                                  c_int32, c_int, c_void_p]),
+    "msa_route_scores_workspace": (_STATUS, [c_int32, c_int32, c_int32, c_int32, c_int64, c_int32,
+                                             c_int, POINTER(c_size_t)]),
+    "msa_route_scores": (_STATUS, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
+                                   c_int64, c_int32, c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "msa_topk_docs_workspace": (_STATUS, [c_int32, c_int64, c_int32, POINTER(c_size_t)]),
+    "msa_topk_docs": (_STATUS, [c_void_p, c_int32, c_int64, c_int32, c_void_p, c_void_p, c_void_p,
+                                c_size_t, c_void_p]),
+    "msa_gather_kv": (_STATUS, [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int64,
+                                c_int32, c_int32, c_int32, c_int, c_void_p, c_void_p, c_int32,
+                                c_void_p]),
+    "msa_sparse_attn_workspace": (_STATUS, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                            c_int32, c_int, POINTER(c_size_t)]),
+    "msa_sparse_attn": (_STATUS, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
+                                  c_int32, c_int32, c_int32, c_int32, c_int32, c_float, c_int,
+                                  c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+}
+
+
+class MsaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"libmsa status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libmsa.so (built in-tree by ``python -m routed_sparse_attention_msa_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run python -m routed_sparse_attention_msa_amd.build")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status):
+    if status != MSA_OK:
+        raise MsaError(status, lib().msa_last_error().decode())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return MSA_F32
+    if t.dtype == torch.bfloat16:
+        return MSA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _dev(t, name, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (the HIP path has no CPU fallback)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _workspace(nbytes, device, ws):
+    if nbytes == 0:
+        return None, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    elif ws.numel() * ws.element_size() < nbytes:
+        raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, needs {nbytes}")
+    return ws, ws.numel() * ws.element_size()
+
+
+# ---------------------------------------------------------------------------
+# S1
+# ---------------------------------------------------------------------------
+
+def msa_pool_chunks(x, chunk, xbar=None, xbar_norm=None, with_norm=False):
+    """Chunk-mean pool ``x`` [n_docs, doc_len, heads, dim] -> (xbar [n_docs*C, heads, dim],
+    xbar_norm [n_docs*C, heads] float32 or None)."""
+    _dev(x, "x", ndim=4)
+    n_docs, doc_len, heads, dim = x.shape
+    if doc_len % chunk:
+        raise ValueError("doc_len must be a multiple of chunk")
+    n_ch = n_docs * (doc_len // chunk)
+    if xbar is None:
+        xbar = torch.empty((n_ch, heads, dim), dtype=x.dtype, device=x.device)
+    _dev(xbar, "xbar", dtype=x.dtype)
+    if xbar.shape != (n_ch, heads, dim):
+        raise ValueError(f"xbar must be {(n_ch, heads, dim)}")
+    if with_norm and xbar_norm is None:
+        xbar_norm = torch.empty((n_ch, heads), dtype=torch.float32, device=x.device)
+    if xbar_norm is not None:
+        _dev(xbar_norm, "xbar_norm", dtype=torch.float32)
+        if xbar_norm.shape != (n_ch, heads):
+            raise ValueError(f"xbar_norm must be {(n_ch, heads)}")
+    _check(lib().msa_pool_chunks(_ptr(x), _ptr(xbar), _ptr(xbar_norm), n_docs, doc_len, chunk, heads,
+                                 dim, _dtype_code(x), _stream(x.device)))
+    return xbar, xbar_norm
+
+
+# ---------------------------------------------------------------------------
+# S2
+# ---------------------------------------------------------------------------
+
+def msa_route_scores_workspace(batch, q_len, heads, dim, n_docs, chunks_per_doc, dtype):
+    n = c_size_t(0)
+    code = MSA_F32 if dtype == torch.float32 else MSA_BF16
+    _check(lib().msa_route_scores_workspace(batch, q_len, heads, dim, n_docs, chunks_per_doc, code,
+                                            ctypes.byref(n)))
+    return n.value
+
+
+def msa_route_scores(q_r, kbar_r, kbar_r_norm, chunks_per_doc, doc_scores=None, ws=None):
+    """Routing scores [batch, n_docs] float32 of router queries ``q_r`` [batch, q_len, heads, dim]
+    against the pooled router keys ``kbar_r`` [n_docs*C, heads, dim] and their norms."""
+    _dev(q_r, "q_r", ndim=4)
+    _dev(kbar_r, "kbar_r", dtype=q_r.dtype, ndim=3)
+    _dev(kbar_r_norm, "kbar_r_norm", dtype=torch.float32, ndim=2)
+    batch, q_len, heads, dim = q_r.shape
+    n_ch = kbar_r.shape[0]
+    if kbar_r.shape[1:] != (heads, dim) or kbar_r_norm.shape != (n_ch, heads):
+        raise ValueError("router query, pooled keys and norms disagree in shape")
+    if n_ch % chunks_per_doc:
+        raise ValueError("chunk count is not a multiple of chunks_per_doc")
+    n_docs = n_ch // chunks_per_doc
+    if doc_scores is None:
+        doc_scores = torch.empty((batch, n_docs), dtype=torch.float32, device=q_r.device)
+    _dev(doc_scores, "doc_scores", dtype=torch.float32)
+    nbytes = msa_route_scores_workspace(batch, q_len, heads, dim, n_docs, chunks_per_doc, q_r.dtype)
+    ws, ws_bytes = _workspace(nbytes, q_r.device, ws)
+    _check(lib().msa_route_scores(_ptr(q_r), _ptr(kbar_r), _ptr(kbar_r_norm), batch, q_len, heads, dim,
+                                  n_docs, chunks_per_doc, _dtype_code(q_r), _ptr(doc_scores), _ptr(ws),
+                                  ws_bytes, _stream(q_r.device)))
+    return doc_scores
+
+
+# ---------------------------------------------------------------------------
+# S3
+# ---------------------------------------------------------------------------
+
+def msa_topk_docs_workspace(batch, n_docs, k):
+    n = c_size_t(0)
+    _check(lib().msa_topk_docs_workspace(batch, n_docs, k, ctypes.byref(n)))
+    return n.value
+
+
+def msa_topk_docs(doc_scores, k, topk_ids=None, topk_scores=None, with_scores=True, ws=None):
+    """Top-k document ids [batch, k] int32 (and scores) of ``doc_scores`` [batch, n_docs]."""
+    _dev(doc_scores, "doc_scores", dtype=torch.float32, ndim=2)
+    batch, n_docs = doc_scores.shape
+    if topk_ids is None:
+        topk_ids = torch.empty((batch, k), dtype=torch.int32, device=doc_scores.device)
+    _dev(topk_ids, "topk_ids", dtype=torch.int32)
+    if with_scores and topk_scores is None:
+        topk_scores = torch.empty((batch, k), dtype=torch.float32, device=doc_scores.device)
+    if topk_scores is not None:
+        _dev(topk_scores, "topk_scores", dtype=torch.float32)
+    ws, ws_bytes = _workspace(msa_topk_docs_workspace(batch, n_docs, k), doc_scores.device, ws)
+    _check(lib().msa_topk_docs(_ptr(doc_scores), batch, n_docs, k, _ptr(topk_ids), _ptr(topk_scores),
+                               _ptr(ws), ws_bytes, _stream(doc_scores.device)))
+    return topk_ids, topk_scores
+
+
+# ---------------------------------------------------------------------------
+# S4
+# ---------------------------------------------------------------------------
+
+def msa_gather_kv(kbar, vbar, topk_ids, chunks_per_doc, k_sel=None, v_sel=None, checked=False,
+                  host_memcpy=False):
+    """Gather the selected documents' pooled K/V -> (k_sel, v_sel) [batch, k*C, heads_kv, dim].
+
+    ``kbar``/``vbar`` [n_docs*C, heads_kv, dim] are GPU tensors, or pinned CPU
+    tensors (host tier: read by the GPU over the host link, or copied per
+    document with ``host_memcpy=True``)."""
+    on_host = not kbar.is_cuda
+    for name, t in (("kbar", kbar), ("vbar", vbar)):
+        if on_host:
+            if not t.is_pinned():
+                raise ValueError(f"{name} on the host must be pinned memory")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+        else:
+            _dev(t, name, ndim=3)
+    if vbar.dtype != kbar.dtype or vbar.shape != kbar.shape or vbar.is_cuda != kbar.is_cuda:
+        raise ValueError("kbar and vbar must match")
+    _dev(topk_ids, "topk_ids", dtype=torch.int32, ndim=2)
+    n_ch, heads_kv, dim = kbar.shape
+    batch, k = topk_ids.shape
+    n_docs = n_ch // chunks_per_doc
+    shape = (batch, k * chunks_per_doc, heads_kv, dim)
+    dev = topk_ids.device
+    if k_sel is None:
+        k_sel = torch.empty(shape, dtype=kbar.dtype, device=dev)
+    if v_sel is None:
+        v_sel = torch.empty(shape, dtype=kbar.dtype, device=dev)
+    _dev(k_sel, "k_sel", dtype=kbar.dtype)
+    _dev(v_sel, "v_sel", dtype=kbar.dtype)
+    flags = (MSA_GATHER_CHECKED if checked else 0) | (MSA_GATHER_HOST_MEMCPY if host_memcpy else 0)
+    _check(lib().msa_gather_kv(_ptr(kbar), _ptr(vbar), 1 if on_host else 0, _ptr(topk_ids), batch, k,
+                               n_docs, chunks_per_doc, heads_kv, dim, _dtype_code(kbar), _ptr(k_sel),
+                               _ptr(v_sel), flags, _stream(dev)))
+    return k_sel, v_sel
+
+
+# ---------------------------------------------------------------------------
+# S5 / S6
+# ---------------------------------------------------------------------------
+
+def msa_sparse_attn_workspace(batch, q_len, heads_q, heads_kv, dim, mem_len, loc_len, dtype):
+    n = c_size_t(0)
+    code = MSA_F32 if dtype == torch.float32 else MSA_BF16
+    _check(lib().msa_sparse_attn_workspace(batch, q_len, heads_q, heads_kv, dim, mem_len, loc_len, code,
+                                           ctypes.byref(n)))
+    return n.value
+
+
+def msa_sparse_attn(q, k_sel, v_sel, k_loc, v_loc, scale=None, out=None, lse=None, with_lse=True,
+                    ws=None):
+    """Sparse GQA attention of ``q`` [batch, q_len, heads_q, dim] over
+    [k_sel/v_sel [batch, mem_len, heads_kv, dim] ; causal k_loc/v_loc [batch, loc_len, heads_kv, dim]]
+    -> (out [batch, q_len, heads_q, dim], lse [batch, heads_q, q_len] float32 or None)."""
+    _dev(q, "q", ndim=4)
+    _dev(k_loc, "k_loc", dtype=q.dtype, ndim=4)
+    _dev(v_loc, "v_loc", dtype=q.dtype, ndim=4)
+    batch, q_len, heads_q, dim = q.shape
+    loc_len, heads_kv = k_loc.shape[1], k_loc.shape[2]
+    if k_sel is None:
+        mem_len = 0
+    else:
+        _dev(k_sel, "k_sel", dtype=q.dtype, ndim=4)
+        _dev(v_sel, "v_sel", dtype=q.dtype, ndim=4)
+        mem_len = k_sel.shape[1]
+        if k_sel.shape != (batch, mem_len, heads_kv, dim) or v_sel.shape != k_sel.shape:
+            raise ValueError("k_sel/v_sel shape mismatch")
+    if k_loc.shape != (batch, loc_len, heads_kv, dim) or v_loc.shape != k_loc.shape:
+        raise ValueError("k_loc/v_loc shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dim)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", dtype=q.dtype)
+    if with_lse and lse is None:
+        lse = torch.empty((batch, heads_q, q_len), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev(lse, "lse", dtype=torch.float32)
+    nbytes = msa_sparse_attn_workspace(batch, q_len, heads_q, heads_kv, dim, mem_len, loc_len, q.dtype)
+    ws, ws_bytes = _workspace(nbytes, q.device, ws)
+    _check(lib().msa_sparse_attn(_ptr(q), _ptr(k_sel), _ptr(v_sel), mem_len, _ptr(k_loc), _ptr(v_loc),
+                                 loc_len, batch, q_len, heads_q, heads_kv, dim, float(scale),
+                                 _dtype_code(q), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
+                                 _stream(q.device)))
+    return out, lse

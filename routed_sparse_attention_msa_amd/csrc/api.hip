@@ -1,0 +1,331 @@
+// The extern "C" boundary of libmsa: argument validation, workspace sizing,
+// error reporting, and the host-tier fetch engine.  Every compute step runs
+// in the HIP kernels behind the launch_* functions.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error = "no error";
+
+msa_status fail(msa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+msa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MSA_OK;
+  return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t dtype_size(msa_dtype dt) { return dt == MSA_F32 ? 4 : 2; }
+
+bool valid_dtype(int dt) { return dt == MSA_F32 || dt == MSA_BF16; }
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+#define CHECK_ARG(cond, ...)                                   \
+  do {                                                         \
+    if (!(cond)) return fail(MSA_ERR_INVALID, __VA_ARGS__);    \
+  } while (0)
+
+// Library-owned, per-device resources for the host tier.  Created on first
+// use, kept until the process ends.
+struct DeviceRes {
+  int* err_flag = nullptr;
+  hipStream_t side = nullptr;
+  hipEvent_t copy_done = nullptr;
+  int32_t* host_ids = nullptr;
+  size_t host_ids_cap = 0;
+};
+std::mutex g_res_mutex;
+std::vector<DeviceRes> g_res;
+
+msa_status device_res(DeviceRes** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_res_mutex);
+  if ((int)g_res.size() <= dev) g_res.resize(dev + 1);
+  DeviceRes& r = g_res[dev];
+  if (r.err_flag == nullptr) {
+    if ((e = hipMalloc(&r.err_flag, sizeof(int))) != hipSuccess) return hip_status(e, "hipMalloc(flag)");
+    if ((e = hipStreamCreateWithFlags(&r.side, hipStreamNonBlocking)) != hipSuccess)
+      return hip_status(e, "hipStreamCreate");
+    if ((e = hipEventCreateWithFlags(&r.copy_done, hipEventDisableTiming)) != hipSuccess)
+      return hip_status(e, "hipEventCreate");
+  }
+  *out = &r;
+  return MSA_OK;
+}
+
+// Device-visible address of pinned host memory, or an error for pageable memory.
+msa_status host_device_ptr(const void* p, const void** dptr) {
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MSA_ERR_INVALID, "host-tier source %p is not pinned host memory", p);
+  }
+  if (attr.type != hipMemoryTypeHost)
+    return fail(MSA_ERR_INVALID, "host-tier source %p is not pinned host memory (type %d)", p,
+                (int)attr.type);
+  *dptr = attr.devicePointer != nullptr ? attr.devicePointer : p;
+  return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int msa_abi_version(void) { return 1; }
+
+const char* msa_last_error(void) { return g_last_error.c_str(); }
+
+// ---------------------------------------------------------------------------
+msa_status msa_pool_chunks(const void* x, void* xbar, float* xbar_norm, int64_t n_docs,
+                           int32_t doc_len, int32_t chunk, int32_t heads, int32_t dim,
+                           msa_dtype dt, void* stream) {
+  CHECK_ARG(valid_dtype(dt), "unknown dtype %d", (int)dt);
+  CHECK_ARG(n_docs >= 0 && doc_len > 0 && chunk > 0 && heads > 0 && dim > 0,
+            "sizes must be positive (n_docs=%lld doc_len=%d chunk=%d heads=%d dim=%d)",
+            (long long)n_docs, doc_len, chunk, heads, dim);
+  CHECK_ARG(doc_len % chunk == 0, "doc_len %d is not a multiple of chunk %d", doc_len, chunk);
+  const size_t es = dtype_size(dt);
+  CHECK_ARG(((size_t)heads * dim * es) % 16 == 0, "heads*dim*sizeof(dtype) must be a multiple of 16");
+  if (xbar_norm != nullptr) {
+    const int64_t hb = (int64_t)dim * (int64_t)es;
+    CHECK_ARG(is_pow2(hb) && hb >= 16 && hb <= 1024,
+              "with norms, dim*sizeof(dtype) must be a power of two in [16, 1024] (got %lld)",
+              (long long)hb);
+    CHECK_ARG(aligned16(xbar_norm) || ((uintptr_t)xbar_norm & 3u) == 0, "xbar_norm misaligned");
+  }
+  if (n_docs == 0) return MSA_OK;
+  CHECK_ARG(x && xbar, "null tensor pointer");
+  CHECK_ARG(aligned16(x) && aligned16(xbar), "x and xbar must be 16-byte aligned");
+  const int64_t n_chunks = n_docs * (doc_len / chunk);
+  CHECK_ARG(n_chunks < (int64_t)1 << 31, "too many chunks");
+  return hip_status(msa::launch_pool(x, xbar, xbar_norm, n_chunks, chunk, heads, dim, dt,
+                                     static_cast<hipStream_t>(stream)),
+                    "msa_pool_chunks launch");
+}
+
+// ---------------------------------------------------------------------------
+static msa_status check_route(int32_t batch, int32_t q_len, int32_t heads, int32_t dim,
+                              int64_t n_docs, int32_t cpd, msa_dtype dt) {
+  CHECK_ARG(valid_dtype(dt), "unknown dtype %d", (int)dt);
+  CHECK_ARG(batch > 0 && q_len > 0 && heads > 0 && dim > 0 && n_docs > 0 && cpd > 0,
+            "sizes must be positive");
+  CHECK_ARG(n_docs < (int64_t)1 << 31 && n_docs * cpd < (int64_t)1 << 31, "bank too large");
+  CHECK_ARG(((size_t)dim * dtype_size(dt)) % 16 == 0, "dim*sizeof(dtype) must be a multiple of 16");
+  return MSA_OK;
+}
+
+msa_status msa_route_scores_workspace(int32_t batch, int32_t q_len, int32_t heads, int32_t dim,
+                                      int64_t n_docs, int32_t chunks_per_doc, msa_dtype dt,
+                                      size_t* bytes) {
+  msa_status st = check_route(batch, q_len, heads, dim, n_docs, chunks_per_doc, dt);
+  if (st != MSA_OK) return st;
+  CHECK_ARG(bytes != nullptr, "bytes is null");
+  *bytes = msa::route_workspace_bytes(batch, q_len, heads, dim, n_docs, chunks_per_doc, dt);
+  return MSA_OK;
+}
+
+msa_status msa_route_scores(const void* q_r, const void* kbar_r, const float* kbar_r_norm,
+                            int32_t batch, int32_t q_len, int32_t heads, int32_t dim,
+                            int64_t n_docs, int32_t chunks_per_doc, msa_dtype dt,
+                            float* doc_scores, void* ws, size_t ws_bytes, void* stream) {
+  msa_status st = check_route(batch, q_len, heads, dim, n_docs, chunks_per_doc, dt);
+  if (st != MSA_OK) return st;
+  CHECK_ARG(q_r && kbar_r && kbar_r_norm && doc_scores, "null tensor pointer");
+  CHECK_ARG(aligned16(q_r) && aligned16(kbar_r) && aligned16(kbar_r_norm) && aligned16(doc_scores),
+            "tensors must be 16-byte aligned");
+  const size_t need = msa::route_workspace_bytes(batch, q_len, heads, dim, n_docs, chunks_per_doc, dt);
+  CHECK_ARG(ws_bytes >= need, "workspace too small (%zu < %zu bytes)", ws_bytes, need);
+  CHECK_ARG(need == 0 || (ws != nullptr && aligned16(ws)), "workspace pointer missing or misaligned");
+  return hip_status(msa::launch_route(q_r, kbar_r, kbar_r_norm, batch, q_len, heads, dim, n_docs,
+                                      chunks_per_doc, dt, doc_scores, ws,
+                                      static_cast<hipStream_t>(stream)),
+                    "msa_route_scores launch");
+}
+
+// ---------------------------------------------------------------------------
+static msa_status check_topk(int32_t batch, int64_t n_docs, int32_t k) {
+  CHECK_ARG(batch > 0 && n_docs > 0, "sizes must be positive");
+  CHECK_ARG(n_docs < (int64_t)1 << 31, "n_docs must be below 2^31");
+  CHECK_ARG(k >= 1 && k <= n_docs && k <= 1024, "k=%d must lie in [1, min(n_docs, 1024)]", k);
+  return MSA_OK;
+}
+
+msa_status msa_topk_docs_workspace(int32_t batch, int64_t n_docs, int32_t k, size_t* bytes) {
+  msa_status st = check_topk(batch, n_docs, k);
+  if (st != MSA_OK) return st;
+  CHECK_ARG(bytes != nullptr, "bytes is null");
+  *bytes = msa::topk_workspace_bytes(batch, n_docs, k);
+  return MSA_OK;
+}
+
+msa_status msa_topk_docs(const float* doc_scores, int32_t batch, int64_t n_docs, int32_t k,
+                         int32_t* topk_ids, float* topk_scores, void* ws, size_t ws_bytes,
+                         void* stream) {
+  msa_status st = check_topk(batch, n_docs, k);
+  if (st != MSA_OK) return st;
+  CHECK_ARG(doc_scores && topk_ids, "null tensor pointer");
+  const size_t need = msa::topk_workspace_bytes(batch, n_docs, k);
+  CHECK_ARG(ws_bytes >= need, "workspace too small (%zu < %zu bytes)", ws_bytes, need);
+  CHECK_ARG(need == 0 || (ws != nullptr && aligned16(ws)), "workspace pointer missing or misaligned");
+  return hip_status(msa::launch_topk(doc_scores, batch, n_docs, k, topk_ids, topk_scores, ws,
+                                     static_cast<hipStream_t>(stream)),
+                    "msa_topk_docs launch");
+}
+
+// ---------------------------------------------------------------------------
+msa_status msa_gather_kv(const void* kbar, const void* vbar, int32_t src_on_host,
+                         const int32_t* topk_ids, int32_t batch, int32_t k, int64_t n_docs,
+                         int32_t chunks_per_doc, int32_t heads_kv, int32_t dim, msa_dtype dt,
+                         void* k_sel, void* v_sel, int32_t flags, void* stream) {
+  CHECK_ARG(valid_dtype(dt), "unknown dtype %d", (int)dt);
+  CHECK_ARG(batch > 0 && k > 0 && n_docs > 0 && chunks_per_doc > 0 && heads_kv > 0 && dim > 0,
+            "sizes must be positive");
+  CHECK_ARG((flags & ~(MSA_GATHER_CHECKED | MSA_GATHER_HOST_MEMCPY)) == 0, "unknown flags 0x%x", flags);
+  CHECK_ARG(kbar && vbar && topk_ids && k_sel && v_sel, "null tensor pointer");
+  const size_t row_bytes = (size_t)heads_kv * dim * dtype_size(dt);
+  CHECK_ARG(row_bytes % 16 == 0, "heads_kv*dim*sizeof(dtype) must be a multiple of 16");
+  CHECK_ARG(aligned16(kbar) && aligned16(vbar) && aligned16(k_sel) && aligned16(v_sel),
+            "tensors must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t doc_bytes = (size_t)chunks_per_doc * row_bytes;
+  hipError_t e;
+
+  if (src_on_host && (flags & MSA_GATHER_HOST_MEMCPY)) {
+    // Per-document copies on the side stream: the ids must be on the host first.
+    const void* dk;
+    const void* dv;
+    msa_status st = host_device_ptr(kbar, &dk);
+    if (st != MSA_OK) return st;
+    if ((st = host_device_ptr(vbar, &dv)) != MSA_OK) return st;
+    DeviceRes* res = nullptr;
+    if ((st = device_res(&res)) != MSA_OK) return st;
+    std::lock_guard<std::mutex> lock(g_res_mutex);
+    const size_t n_ids = (size_t)batch * k;
+    if (res->host_ids_cap < n_ids) {
+      if (res->host_ids) (void)hipHostFree(res->host_ids);
+      res->host_ids = nullptr;
+      if ((e = hipHostMalloc(&res->host_ids, n_ids * sizeof(int32_t), hipHostMallocDefault)) != hipSuccess)
+        return hip_status(e, "hipHostMalloc(ids)");
+      res->host_ids_cap = n_ids;
+    }
+    if ((e = hipMemcpyAsync(res->host_ids, topk_ids, n_ids * sizeof(int32_t), hipMemcpyDeviceToHost, s)) != hipSuccess)
+      return hip_status(e, "ids D2H");
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_status(e, "ids sync");
+    for (size_t i = 0; i < n_ids; ++i) {
+      const int64_t id = res->host_ids[i];
+      if (id < 0 || id >= n_docs)
+        return fail(MSA_ERR_INVALID, "document id %lld at position %zu out of range [0, %lld)",
+                    (long long)id, i, (long long)n_docs);
+    }
+    const char* hk = static_cast<const char*>(kbar);
+    const char* hv = static_cast<const char*>(vbar);
+    for (size_t i = 0; i < n_ids; ++i) {
+      const size_t src = (size_t)res->host_ids[i] * doc_bytes;
+      const size_t dst = i * doc_bytes;
+      if ((e = hipMemcpyAsync(static_cast<char*>(k_sel) + dst, hk + src, doc_bytes,
+                              hipMemcpyHostToDevice, res->side)) != hipSuccess)
+        return hip_status(e, "K fetch");
+      if ((e = hipMemcpyAsync(static_cast<char*>(v_sel) + dst, hv + src, doc_bytes,
+                              hipMemcpyHostToDevice, res->side)) != hipSuccess)
+        return hip_status(e, "V fetch");
+    }
+    if ((e = hipEventRecord(res->copy_done, res->side)) != hipSuccess) return hip_status(e, "event record");
+    if ((e = hipStreamWaitEvent(s, res->copy_done, 0)) != hipSuccess) return hip_status(e, "stream wait");
+    return MSA_OK;
+  }
+
+  const void* src_k = kbar;
+  const void* src_v = vbar;
+  if (src_on_host) {
+    msa_status st = host_device_ptr(kbar, &src_k);
+    if (st != MSA_OK) return st;
+    if ((st = host_device_ptr(vbar, &src_v)) != MSA_OK) return st;
+  }
+  int* flag = nullptr;
+  if (flags & MSA_GATHER_CHECKED) {
+    DeviceRes* res = nullptr;
+    msa_status st = device_res(&res);
+    if (st != MSA_OK) return st;
+    flag = res->err_flag;
+    if ((e = hipMemsetAsync(flag, 0, sizeof(int), s)) != hipSuccess) return hip_status(e, "flag clear");
+  }
+  e = msa::launch_gather(src_k, src_v, topk_ids, batch, k, n_docs, chunks_per_doc, row_bytes, k_sel,
+                         v_sel, flag, s);
+  if (e != hipSuccess) return hip_status(e, "msa_gather_kv launch");
+  if (flag != nullptr) {
+    int h_flag = 0;
+    if ((e = hipMemcpyAsync(&h_flag, flag, sizeof(int), hipMemcpyDeviceToHost, s)) != hipSuccess)
+      return hip_status(e, "flag read");
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_status(e, "flag sync");
+    if (h_flag != 0) return fail(MSA_ERR_INVALID, "a document id was outside [0, %lld)", (long long)n_docs);
+  }
+  return MSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+static msa_status check_attn(int32_t batch, int32_t q_len, int32_t heads_q, int32_t heads_kv,
+                             int32_t dim, int32_t mem_len, int32_t loc_len, msa_dtype dt) {
+  CHECK_ARG(valid_dtype(dt), "unknown dtype %d", (int)dt);
+  CHECK_ARG(batch > 0 && q_len > 0 && heads_q > 0 && heads_kv > 0 && dim > 0 && mem_len >= 0,
+            "sizes must be positive");
+  CHECK_ARG(heads_q % heads_kv == 0, "heads_q %d is not a multiple of heads_kv %d", heads_q, heads_kv);
+  CHECK_ARG(loc_len >= q_len, "loc_len %d must be >= q_len %d", loc_len, q_len);
+  CHECK_ARG(dim <= 256, "dim %d above 256 is not supported", dim);
+  CHECK_ARG(((size_t)dim * dtype_size(dt)) % 16 == 0, "dim*sizeof(dtype) must be a multiple of 16");
+  return MSA_OK;
+}
+
+msa_status msa_sparse_attn_workspace(int32_t batch, int32_t q_len, int32_t heads_q,
+                                     int32_t heads_kv, int32_t dim, int32_t mem_len,
+                                     int32_t loc_len, msa_dtype dt, size_t* bytes) {
+  msa_status st = check_attn(batch, q_len, heads_q, heads_kv, dim, mem_len, loc_len, dt);
+  if (st != MSA_OK) return st;
+  CHECK_ARG(bytes != nullptr, "bytes is null");
+  *bytes = msa::attn_workspace_bytes(batch, q_len, heads_q, heads_kv, dim, mem_len, loc_len, dt);
+  return MSA_OK;
+}
+
+msa_status msa_sparse_attn(const void* q, const void* k_sel, const void* v_sel, int32_t mem_len,
+                           const void* k_loc, const void* v_loc, int32_t loc_len, int32_t batch,
+                           int32_t q_len, int32_t heads_q, int32_t heads_kv, int32_t dim,
+                           float scale, msa_dtype dt, void* out, float* lse, void* ws,
+                           size_t ws_bytes, void* stream) {
+  msa_status st = check_attn(batch, q_len, heads_q, heads_kv, dim, mem_len, loc_len, dt);
+  if (st != MSA_OK) return st;
+  CHECK_ARG(q && k_loc && v_loc && out, "null tensor pointer");
+  CHECK_ARG(mem_len == 0 || (k_sel && v_sel), "k_sel/v_sel required when mem_len > 0");
+  CHECK_ARG(aligned16(q) && aligned16(k_loc) && aligned16(v_loc) && aligned16(out) &&
+                (mem_len == 0 || (aligned16(k_sel) && aligned16(v_sel))),
+            "tensors must be 16-byte aligned");
+  CHECK_ARG(scale == scale && scale > 0.f, "scale must be positive");
+  const size_t need = msa::attn_workspace_bytes(batch, q_len, heads_q, heads_kv, dim, mem_len, loc_len, dt);
+  CHECK_ARG(ws_bytes >= need, "workspace too small (%zu < %zu bytes)", ws_bytes, need);
+  CHECK_ARG(need == 0 || (ws != nullptr && aligned16(ws)), "workspace pointer missing or misaligned");
+  return hip_status(msa::launch_attn(q, k_sel, v_sel, mem_len, k_loc, v_loc, loc_len, batch, q_len,
+                                     heads_q, heads_kv, dim, scale, dt, out, lse, ws,
+                                     static_cast<hipStream_t>(stream)),
+                    "msa_sparse_attn launch");
+}
+
+}  // extern "C"

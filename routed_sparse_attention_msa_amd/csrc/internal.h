@@ -1,0 +1,108 @@
+// Internal declarations shared by the libmsa sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/msa.h"
+
+namespace msa {
+
+// ---------------------------------------------------------------------------
+// vector types for gfx950 MFMA operands and 16-byte memory traffic
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// bf16 <-> f32
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round-to-nearest-even float32 -> bf16 bits: add 0x7FFF plus the lowest kept
+// bit, then truncate.  Exact RNE for every finite input (overflow goes to inf).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Element traits for the two storage dtypes.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ float to_f32(float v) { return v; }
+  static __device__ __forceinline__ float from_f32(float v) { return v; }
+};
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ float to_f32(uint16_t v) { return bf16_to_f32(v); }
+  static __device__ __forceinline__ uint16_t from_f32(float v) { return f32_to_bf16(v); }
+};
+
+// 16 bytes of elements, widened to float32.
+template <typename T> struct Vec16;
+template <> struct Vec16<float> {
+  static constexpr int N = 4;
+  static __device__ __forceinline__ void widen(const u32x4& raw, float* out) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(raw[i]);
+  }
+  static __device__ __forceinline__ u32x4 narrow(const float* in) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = __float_as_uint(in[i]);
+    return r;
+  }
+};
+template <> struct Vec16<uint16_t> {
+  static constexpr int N = 8;
+  static __device__ __forceinline__ void widen(const u32x4& raw, float* out) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(raw[i] << 16);
+      out[2 * i + 1] = __uint_as_float(raw[i] & 0xFFFF0000u);
+    }
+  }
+  static __device__ __forceinline__ u32x4 narrow(const float* in) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      r[i] = (uint32_t)f32_to_bf16(in[2 * i]) | ((uint32_t)f32_to_bf16(in[2 * i + 1]) << 16);
+    return r;
+  }
+};
+
+__device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void store16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// ---------------------------------------------------------------------------
+// launchers (each returns hipGetLastError() of its launches)
+// ---------------------------------------------------------------------------
+hipError_t launch_pool(const void* x, void* xbar, float* norm, int64_t n_chunks, int chunk,
+                       int heads, int dim, msa_dtype dt, hipStream_t s);
+
+size_t route_workspace_bytes(int batch, int q_len, int heads, int dim, int64_t n_docs, int cpd,
+                             msa_dtype dt);
+hipError_t launch_route(const void* q_r, const void* kbar_r, const float* knorm, int batch,
+                        int q_len, int heads, int dim, int64_t n_docs, int cpd, msa_dtype dt,
+                        float* doc_scores, void* ws, hipStream_t s);
+
+size_t topk_workspace_bytes(int batch, int64_t n_docs, int k);
+hipError_t launch_topk(const float* scores, int batch, int64_t n_docs, int k, int32_t* ids,
+                       float* vals, void* ws, hipStream_t s);
+
+hipError_t launch_gather(const void* kbar, const void* vbar, const int32_t* ids, int batch, int k,
+                         int64_t n_docs, int cpd, size_t row_bytes, void* k_sel, void* v_sel,
+                         int* err_flag, hipStream_t s);
+
+size_t attn_workspace_bytes(int batch, int q_len, int heads_q, int heads_kv, int dim, int mem_len,
+                            int loc_len, msa_dtype dt);
+hipError_t launch_attn(const void* q, const void* k_sel, const void* v_sel, int mem_len,
+                       const void* k_loc, const void* v_loc, int loc_len, int batch, int q_len,
+                       int heads_q, int heads_kv, int dim, float scale, msa_dtype dt, void* out,
+                       float* lse, void* ws, hipStream_t s);
+
+}  // namespace msa

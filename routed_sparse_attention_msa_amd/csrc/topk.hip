@@ -1,0 +1,232 @@
+// S3: exact top-k document selection.
+//
+// Method: MSA README (EverMind-AI/MSA), "Overall Design" and "Inference
+// Pipeline" stage 2 -- the top-k documents by routing score are selected.
+//
+// Each (score, doc id) pair becomes one unique 64-bit key:
+//     high 32 bits: the score's bits mapped so that unsigned order = float order
+//     low  32 bits: 0xFFFFFFFF - id   (equal scores: the lower id is larger)
+// so "k largest keys" is exactly "k best scores, ties to the lower id", a
+// total order with a unique answer.
+//
+// A workgroup (256 threads x 16 keys = 4096 keys in registers) finds the k
+// largest of its keys with an MSB-first radix select (8-bit digits, an LDS
+// histogram per digit, a suffix scan across the 4 waves with cross-lane
+// shuffles), stopping as soon as the remaining candidates are all selected.
+// The k winners are appended to LDS and ordered with a bitonic network.
+// Rows longer than one tile are reduced in rounds: every tile emits its k
+// best keys to the workspace, and the next round selects among those.
+#include "internal.h"
+
+namespace msa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kItems = 16;
+constexpr int kTile = kThreads * kItems;
+constexpr int kMaxK = 1024;
+
+__device__ __forceinline__ uint32_t order_score(float s) {
+  if (s == 0.f) s = 0.f;  // -0.0 and +0.0 compare equal: give them one key
+  const uint32_t u = __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float unorder_score(uint32_t o) {
+  const uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t make_key(float s, uint32_t id) {
+  return ((uint64_t)order_score(s) << 32) | (uint64_t)(0xFFFFFFFFu - id);
+}
+
+struct Smem {
+  uint64_t list[kMaxK];
+  uint32_t hist[256];
+  uint32_t wave_sum[kThreads / 64];
+  uint32_t count;
+  uint32_t sel_digit, sel_gt, sel_cnt;
+};
+
+// Inclusive prefix sum of one value per thread over the block.
+__device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, Smem& sm) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(v, off);
+    if (lane >= off) v += y;
+  }
+  if (lane == 63) sm.wave_sum[wave] = v;
+  __syncthreads();
+  uint32_t base = 0;
+  for (int w = 0; w < wave; ++w) base += sm.wave_sum[w];
+  __syncthreads();
+  return v + base;
+}
+
+// The block holds kItems keys per thread (`valid` marks real ones; real keys
+// are unique).  Leaves the min(k, #valid) largest keys sorted in descending
+// order in sm.list[0 .. kp2), padded with 0 (below every real key).
+__device__ void block_select(const uint64_t (&key)[kItems], const bool (&valid)[kItems], int k,
+                             int kp2, Smem& sm) {
+  const int tid = threadIdx.x;
+  uint32_t my_valid = 0;
+#pragma unroll
+  for (int i = 0; i < kItems; ++i) my_valid += valid[i] ? 1u : 0u;
+  const uint32_t n_valid = block_inclusive_scan(my_valid, sm);
+  if (tid == kThreads - 1) sm.count = n_valid;  // total
+  __syncthreads();
+  const int k_eff = (int)min((uint32_t)k, sm.count);
+  __syncthreads();
+
+  uint64_t prefix = 0, mask = 0;
+  int krem = k_eff;
+  if (k_eff > 0) {
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      sm.hist[tid] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kItems; ++i)
+        if (valid[i] && (key[i] & mask) == prefix) atomicAdd(&sm.hist[(key[i] >> shift) & 0xFF], 1u);
+      __syncthreads();
+      // Thread t looks at bin 255 - t: the inclusive scan is then the number
+      // of candidates whose digit is >= that bin.
+      const uint32_t bin = 255 - tid;
+      const uint32_t h = sm.hist[bin];
+      const uint32_t incl = block_inclusive_scan(h, sm);
+      const uint32_t excl = incl - h;
+      if (excl < (uint32_t)krem && (uint32_t)krem <= incl) {
+        sm.sel_digit = bin;
+        sm.sel_gt = excl;
+        sm.sel_cnt = h;
+      }
+      __syncthreads();
+      prefix |= (uint64_t)sm.sel_digit << shift;
+      mask |= (uint64_t)0xFF << shift;
+      krem -= (int)sm.sel_gt;
+      const bool done = (int)sm.sel_cnt == krem;  // every key with this prefix is in
+      __syncthreads();
+      if (done) break;
+    }
+  }
+
+  if (tid == 0) sm.count = 0;
+  __syncthreads();
+  if (k_eff > 0) {
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      if (valid[i] && (key[i] & mask) >= prefix) {
+        const uint32_t pos = atomicAdd(&sm.count, 1u);
+        sm.list[pos] = key[i];
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = k_eff + tid; i < kp2; i += kThreads) sm.list[i] = 0;
+  __syncthreads();
+
+  // Bitonic sort of sm.list[0 .. kp2), descending.
+  for (int size = 2; size <= kp2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < kp2 / 2; i += kThreads) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const uint64_t a = sm.list[lo], b = sm.list[hi];
+        if ((a < b) == desc) {
+          sm.list[lo] = b;
+          sm.list[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// One tile of one row.  FROM_KEYS: the input is a previous round's keys
+// (0 = padding); otherwise raw float scores whose ids are their positions.
+// FINAL: write ids/scores; otherwise write the tile's k best keys.
+template <bool FROM_KEYS, bool FINAL>
+__global__ __launch_bounds__(kThreads) void topk_tile_kernel(
+    const float* __restrict__ scores, const uint64_t* __restrict__ keys_in, int64_t n, int k,
+    int kp2, uint64_t* __restrict__ keys_out, int32_t* __restrict__ ids_out,
+    float* __restrict__ vals_out) {
+  __shared__ Smem sm;
+  const int b = blockIdx.y;
+  const int64_t base = (int64_t)blockIdx.x * kTile;
+  uint64_t key[kItems];
+  bool valid[kItems];
+#pragma unroll
+  for (int i = 0; i < kItems; ++i) {
+    const int64_t idx = base + i * kThreads + threadIdx.x;
+    valid[i] = idx < n;
+    key[i] = 0;
+    if (valid[i]) {
+      if (FROM_KEYS) {
+        key[i] = keys_in[(size_t)b * n + idx];
+        valid[i] = key[i] != 0;
+      } else {
+        key[i] = make_key(scores[(size_t)b * n + idx], (uint32_t)idx);
+      }
+    }
+  }
+  block_select(key, valid, k, kp2, sm);
+  for (int i = threadIdx.x; i < k; i += kThreads) {
+    const uint64_t kk = sm.list[i];
+    if (FINAL) {
+      ids_out[(size_t)b * k + i] = (int32_t)(0xFFFFFFFFu - (uint32_t)kk);
+      if (vals_out) vals_out[(size_t)b * k + i] = unorder_score((uint32_t)(kk >> 32));
+    } else {
+      keys_out[((size_t)b * gridDim.x + blockIdx.x) * k + i] = kk;
+    }
+  }
+}
+
+inline int next_pow2(int v) {
+  int p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+}  // namespace
+
+size_t topk_workspace_bytes(int batch, int64_t n_docs, int k) {
+  const int64_t tiles = (n_docs + kTile - 1) / kTile;
+  if (tiles <= 1) return 0;
+  return 2 * (size_t)batch * (size_t)tiles * (size_t)k * sizeof(uint64_t);
+}
+
+hipError_t launch_topk(const float* scores, int batch, int64_t n_docs, int k, int32_t* ids,
+                       float* vals, void* ws, hipStream_t s) {
+  const int kp2 = next_pow2(k);
+  int64_t tiles = (n_docs + kTile - 1) / kTile;
+  if (tiles <= 1) {
+    hipLaunchKernelGGL((topk_tile_kernel<false, true>), dim3(1, batch), dim3(kThreads), 0, s,
+                       scores, nullptr, n_docs, k, kp2, nullptr, ids, vals);
+    return hipGetLastError();
+  }
+  uint64_t* buf[2];
+  buf[0] = static_cast<uint64_t*>(ws);
+  buf[1] = buf[0] + (size_t)batch * (size_t)tiles * (size_t)k;
+  hipLaunchKernelGGL((topk_tile_kernel<false, false>), dim3((unsigned)tiles, batch), dim3(kThreads),
+                     0, s, scores, nullptr, n_docs, k, kp2, buf[0], nullptr, nullptr);
+  int cur = 0;
+  int64_t n = tiles * k;
+  for (;;) {
+    tiles = (n + kTile - 1) / kTile;
+    if (tiles == 1) {
+      hipLaunchKernelGGL((topk_tile_kernel<true, true>), dim3(1, batch), dim3(kThreads), 0, s,
+                         nullptr, buf[cur], n, k, kp2, nullptr, ids, vals);
+      break;
+    }
+    hipLaunchKernelGGL((topk_tile_kernel<true, false>), dim3((unsigned)tiles, batch),
+                       dim3(kThreads), 0, s, nullptr, buf[cur], n, k, kp2, buf[cur ^ 1], nullptr,
+                       nullptr);
+    cur ^= 1;
+    n = tiles * k;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -1,0 +1,117 @@
+"""The C-ABI library loads, exports every entry point include/msa.h declares,
+and rejects invalid arguments on the host (no GPU work is enqueued by any of
+these calls)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import routed_sparse_attention_msa_amd as msa
+from routed_sparse_attention_msa_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding():
+    assert _declared() == sorted(L.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r" T (msa_\w+)", out))
+    missing = [s for s in _declared() if s not in exported]
+    assert not missing, missing
+
+
+def test_loads_and_reports_version():
+    lib = msa.lib()
+    assert lib.msa_abi_version() == 1
+    for name in _declared():
+        assert hasattr(lib, name)
+
+
+def _err():
+    return msa.lib().msa_last_error().decode()
+
+
+def test_pool_validation():
+    lib = msa.lib()
+    p = ctypes.c_void_p(16)
+    # doc_len not a multiple of chunk
+    assert lib.msa_pool_chunks(p, p, None, 4, 100, 64, 8, 128, L.MSA_BF16, None) == L.MSA_ERR_INVALID
+    assert "multiple of chunk" in _err()
+    # unknown dtype
+    assert lib.msa_pool_chunks(p, p, None, 4, 512, 64, 8, 128, 7, None) == L.MSA_ERR_INVALID
+    # misaligned pointer
+    q = ctypes.c_void_p(18)
+    assert lib.msa_pool_chunks(q, p, None, 4, 512, 64, 8, 128, L.MSA_BF16, None) == L.MSA_ERR_INVALID
+    assert "aligned" in _err()
+    # norms need a power-of-two head size in bytes
+    assert lib.msa_pool_chunks(p, p, p, 4, 512, 64, 1, 24, L.MSA_BF16, None) == L.MSA_ERR_INVALID
+    # zero documents is a no-op
+    assert lib.msa_pool_chunks(None, None, None, 0, 512, 64, 8, 128, L.MSA_BF16, None) == L.MSA_OK
+
+
+def test_topk_validation_and_workspace():
+    lib = msa.lib()
+    n = ctypes.c_size_t(123)
+    assert lib.msa_topk_docs_workspace(1, 100, 0, ctypes.byref(n)) == L.MSA_ERR_INVALID
+    assert lib.msa_topk_docs_workspace(1, 100, 101, ctypes.byref(n)) == L.MSA_ERR_INVALID
+    assert lib.msa_topk_docs_workspace(1, 5000, 1025, ctypes.byref(n)) == L.MSA_ERR_INVALID
+    assert lib.msa_topk_docs_workspace(1, 4096, 16, ctypes.byref(n)) == L.MSA_OK and n.value == 0
+    assert lib.msa_topk_docs_workspace(4, 195313, 16, ctypes.byref(n)) == L.MSA_OK
+    assert n.value == 2 * 4 * 48 * 16 * 8
+    p = ctypes.c_void_p(256)
+    assert lib.msa_topk_docs(p, 4, 195313, 16, p, None, None, 0, None) == L.MSA_ERR_INVALID
+    assert "workspace" in _err()
+
+
+def test_route_validation():
+    lib = msa.lib()
+    p = ctypes.c_void_p(256)
+    assert lib.msa_route_scores(p, p, None, 1, 8, 8, 128, 16, 8, L.MSA_BF16, p, None, 0, None) == L.MSA_ERR_INVALID
+    assert lib.msa_route_scores(p, p, p, 1, 8, 8, 12, 16, 8, L.MSA_BF16, p, None, 0, None) == L.MSA_ERR_INVALID
+    n = ctypes.c_size_t(0)
+    assert lib.msa_route_scores_workspace(1, 2048, 8, 128, 2048, 8, L.MSA_BF16, ctypes.byref(n)) == L.MSA_OK
+
+
+def test_attn_validation():
+    lib = msa.lib()
+    p = ctypes.c_void_p(256)
+    # heads_q not a multiple of heads_kv
+    assert lib.msa_sparse_attn(p, p, p, 8, p, p, 16, 1, 16, 6, 4, 128, 0.1, L.MSA_BF16, p, None, None, 0,
+                               None) == L.MSA_ERR_INVALID
+    # local KV shorter than the query
+    assert lib.msa_sparse_attn(p, p, p, 8, p, p, 8, 1, 16, 8, 4, 128, 0.1, L.MSA_BF16, p, None, None, 0,
+                               None) == L.MSA_ERR_INVALID
+    # non-positive scale
+    assert lib.msa_sparse_attn(p, p, p, 8, p, p, 16, 1, 16, 8, 4, 128, 0.0, L.MSA_BF16, p, None, None, 0,
+                               None) == L.MSA_ERR_INVALID
+    # memory rows without tensors
+    assert lib.msa_sparse_attn(p, None, None, 8, p, p, 16, 1, 16, 8, 4, 128, 0.1, L.MSA_BF16, p, None, None,
+                               0, None) == L.MSA_ERR_INVALID
+
+
+def test_gather_validation():
+    lib = msa.lib()
+    p = ctypes.c_void_p(256)
+    assert lib.msa_gather_kv(p, p, 0, p, 1, 4, 16, 8, 8, 128, L.MSA_BF16, p, p, 0x10, None) == L.MSA_ERR_INVALID
+    assert lib.msa_gather_kv(p, p, 0, p, 1, 4, 16, 8, 1, 4, L.MSA_BF16, p, p, 0, None) == L.MSA_ERR_INVALID
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros((2, 64, 1, 8), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        msa.msa_pool_chunks(x, 64)

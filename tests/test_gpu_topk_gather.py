@@ -1,0 +1,141 @@
+"""GPU parity of S3 (top-k) and S4 (gather, device and host tier), through the C ABI."""
+
+import numpy as np
+import pytest
+import torch
+
+import routed_sparse_attention_msa_amd as msa
+from oracle import gather_kv, topk_docs
+from tests.parity import case, to_f64, topk_band_check
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _gpu_topk(scores, k):
+    ids, vals = msa.msa_topk_docs(scores, k)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), vals.cpu().numpy()
+
+
+@pytest.mark.parametrize("batch,n,k", [
+    (1, 64, 4), (1, 2048, 16), (32, 2048, 16), (1, 4096, 16), (2, 4097, 16), (4, 195313, 16),
+    (1, 19532, 32), (1, 5000, 1024), (3, 1024, 1024), (2, 100, 1), (1, 12289, 300), (2, 1, 1),
+])
+def test_topk_exact(batch, n, k):
+    case(f"topk B={batch} N={n} k={k}")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(n + k)
+    scores = torch.randn((batch, n), generator=g, device=DEV)
+    ids, vals = _gpu_topk(scores, k)
+    ref_ids, ref_vals = topk_docs(to_f64(scores), k)
+    # same input scores on both sides: the selection is exact (integer work)
+    assert np.array_equal(ids, ref_ids)
+    assert np.array_equal(vals.astype(np.float64), ref_vals)
+
+
+def test_topk_ties_and_signed_zero():
+    case("topk ties")
+    s = torch.zeros((2, 5000), device=DEV)
+    s[0, ::7] = -0.0                     # -0.0 ties with +0.0: lower ids first
+    s[0, 1000:1010] = 1.0
+    s[1] = torch.tensor([0.5, -0.0, 0.0, 0.5] * 1250, device=DEV)
+    ids, vals = _gpu_topk(s, 20)
+    ref_ids, ref_vals = topk_docs(to_f64(s), 20)
+    assert np.array_equal(ids, ref_ids)
+    assert ids[0, :10].tolist() == list(range(1000, 1010))
+    assert ids[0, 10:].tolist() == list(range(10))
+    assert ids[1, :4].tolist() == [0, 3, 4, 7]
+
+
+def test_topk_infinities_and_all_equal():
+    case("topk inf")
+    s = torch.full((1, 9000), 0.25, device=DEV)
+    s[0, 17] = float("inf")
+    s[0, 8999] = float("-inf")
+    s[0, 4096] = 0.75
+    ids, _ = _gpu_topk(s, 5)
+    assert ids[0].tolist() == [17, 4096, 0, 1, 2]
+    s2 = torch.full((1, 9000), float("-inf"), device=DEV)
+    ids, _ = _gpu_topk(s2, 3)
+    assert ids[0].tolist() == [0, 1, 2]
+
+
+def test_topk_band_comparator_on_route_like_scores():
+    case("topk band")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    s = (0.3 + 0.03 * torch.randn((8, 2048), generator=g, device=DEV))
+    ids, _ = _gpu_topk(s, 16)
+    ok, exact = topk_band_check(ids, to_f64(s), 16)
+    assert ok and exact
+
+
+def test_topk_deterministic():
+    case("topk determinism")
+    s = torch.randn((4, 50000), device=DEV)
+    a, _ = _gpu_topk(s, 64)
+    b, _ = _gpu_topk(s, 64)
+    assert np.array_equal(a, b)
+
+
+def _bank(n_docs, cpd, heads, dim, dtype, seed):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    kb = torch.randn((n_docs * cpd, heads, dim), generator=g, device=DEV).to(dtype)
+    vb = torch.randn((n_docs * cpd, heads, dim), generator=g, device=DEV).to(dtype)
+    return kb, vb
+
+
+@pytest.mark.parametrize("n_docs,cpd,heads,dim,batch,k,dtype", [
+    (2048, 8, 8, 128, 1, 16, torch.bfloat16),
+    (2048, 8, 8, 128, 32, 32, torch.bfloat16),
+    (64, 8, 2, 64, 1, 4, torch.float32),
+    (10, 3, 1, 8, 2, 10, torch.bfloat16),
+])
+def test_gather_bit_exact(n_docs, cpd, heads, dim, batch, k, dtype):
+    case(f"gather N={n_docs} C={cpd} B={batch} k={k}")
+    kb, vb = _bank(n_docs, cpd, heads, dim, dtype, n_docs + k)
+    ids = torch.stack([torch.randperm(n_docs, device=DEV)[:k] for _ in range(batch)]).to(torch.int32)
+    ks, vs = msa.msa_gather_kv(kb, vb, ids, cpd)
+    torch.cuda.synchronize()
+    raw = torch.int16 if dtype == torch.bfloat16 else torch.int32     # compare bit patterns
+    rk, rv = gather_kv(kb.cpu().view(raw).numpy(), vb.cpu().view(raw).numpy(),
+                       ids.cpu().numpy().astype(np.int64), cpd)
+    assert np.array_equal(ks.cpu().view(raw).numpy(), rk)
+    assert np.array_equal(vs.cpu().view(raw).numpy(), rv)
+
+
+def test_gather_out_of_range_is_zero_and_checked_raises():
+    case("gather out of range")
+    kb, vb = _bank(16, 8, 8, 128, torch.bfloat16, 3)
+    ids = torch.tensor([[3, 16, -1, 15]], dtype=torch.int32, device=DEV)
+    ks, vs = msa.msa_gather_kv(kb, vb, ids, 8)
+    torch.cuda.synchronize()
+    assert torch.equal(ks[0, :8], kb[24:32]) and torch.equal(ks[0, 24:32], kb[120:128])
+    assert not ks[0, 8:24].any() and not vs[0, 8:24].any()
+    with pytest.raises(msa.MsaError, match="outside"):
+        msa.msa_gather_kv(kb, vb, ids, 8, checked=True)
+    ok_ids = torch.tensor([[3, 1]], dtype=torch.int32, device=DEV)
+    msa.msa_gather_kv(kb, vb, ok_ids, 8, checked=True)
+
+
+@pytest.mark.parametrize("host_memcpy", [False, True])
+def test_host_tier_equals_device_gather(host_memcpy):
+    case(f"gather host tier memcpy={host_memcpy}")
+    kb, vb = _bank(512, 8, 8, 128, torch.bfloat16, 11)
+    hk = kb.cpu().pin_memory()
+    hv = vb.cpu().pin_memory()
+    ids = torch.stack([torch.randperm(512, device=DEV)[:16] for _ in range(4)]).to(torch.int32)
+    dk, dv = msa.msa_gather_kv(kb, vb, ids, 8)
+    tk, tv = msa.msa_gather_kv(hk, hv, ids, 8, host_memcpy=host_memcpy)
+    torch.cuda.synchronize()
+    assert torch.equal(dk, tk) and torch.equal(dv, tv)
+
+
+def test_host_tier_rejects_pageable_memory():
+    case("gather pageable")
+    kb = torch.zeros((64, 8, 128), dtype=torch.bfloat16)      # not pinned
+    ids = torch.zeros((1, 2), dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError, match="pinned"):
+        msa.msa_gather_kv(kb, kb, ids, 8)
