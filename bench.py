@@ -1,0 +1,355 @@
+"""Benchmark of the MSA routed-layer hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM:
+
+  prefill (default; the 1M-token bank: 2048 docs x 512 tokens, 32/8 heads,
+           head dim 128, bf16, 2048-token prefill, top-16):
+      pool K, pool V, pool K_r (+norms) -> route -> top-k -> gather -> attention
+  decode  (the same bank; 32 sequences x 1 token, 4096 cached tokens, top-16):
+      route -> top-k -> gather -> split-KV attention (the bank is pooled once,
+      outside the timed region, as the offline stage of the pipeline)
+
+Prints one JSON line.  `value` is query tokens per second of the whole step.
+Per-kernel durations are measured with HIP events on the stream the kernels
+run on; `roofline` describes the kernel with the largest share of the step.
+`cpu_baseline` times the float64 CPU oracle on a bounded sample of the same
+workload and scales it to the full step.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", choices=["prefill", "decode"], default="prefill")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work per launch (bytes that must cross HBM, flops that must be done)
+# ---------------------------------------------------------------------------
+
+def work_pool(cfg, with_norm):
+    rows = cfg.n_doc * cfg.doc_len
+    row_b = cfg.heads_kv * cfg.dim * 2
+    n_ch = cfg.n_chunks
+    b = rows * row_b + n_ch * row_b + (n_ch * cfg.heads_kv * 4 if with_norm else 0)
+    return {"bound": "hbm", "bytes": b, "flops": rows * cfg.heads_kv * cfg.dim}
+
+
+def work_route(cfg):
+    t_tot = cfg.batch * cfg.q_len
+    row = cfg.heads_kv * cfg.dim
+    flops = 2 * t_tot * cfg.n_chunks * row
+    b = cfg.n_chunks * row * 2 + cfg.n_chunks * cfg.heads_kv * 4 + t_tot * row * 2 + cfg.batch * cfg.n_doc * 4
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    return {"bound": "mfma" if flops / b > ridge else "hbm", "bytes": b, "flops": flops}
+
+
+def work_topk(cfg):
+    return {"bound": "hbm", "bytes": cfg.batch * cfg.n_doc * 4 + cfg.batch * cfg.topk * 8, "flops": 0}
+
+
+def work_gather(cfg):
+    b = 2 * 2 * cfg.batch * cfg.mem_len * cfg.heads_kv * cfg.dim * 2 + cfg.batch * cfg.topk * 4
+    return {"bound": "hbm", "bytes": b, "flops": 0}
+
+
+def work_attn(cfg):
+    b_, t_, m, l_ = cfg.batch, cfg.q_len, cfg.mem_len, cfg.loc_len
+    pairs = t_ * m + sum(l_ - t_ + t + 1 for t in range(t_))
+    flops = 4 * cfg.dim * cfg.heads_q * b_ * pairs
+    row_kv = cfg.heads_kv * cfg.dim * 2
+    b = (2 * b_ * t_ * cfg.heads_q * cfg.dim * 2            # q in, o out
+         + 2 * b_ * (m + l_) * row_kv                       # k/v memory + local
+         + b_ * cfg.heads_q * t_ * 4)                       # lse
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    return {"bound": "mfma" if flops / b > ridge else "hbm", "bytes": b, "flops": flops}
+
+
+def roofline_entry(work, ms):
+    s = ms / 1e3
+    if work["bound"] == "mfma":
+        achieved = work["flops"] / s / 1e12
+        return {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / MFMA_BF16_PEAK_TFLOPS}
+    achieved = work["bytes"] / s / 1e9
+    return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS}
+
+
+# ---------------------------------------------------------------------------
+# measured HBM traffic (rocprofv3 counters), valid only for the source it was taken on
+# ---------------------------------------------------------------------------
+
+def kernel_source_sha(src_file):
+    path = os.path.join(ROOT, "routed_sparse_attention_msa_amd", "csrc", src_file)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(stage, src_file, launches_per_step):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(stage)
+    if not rec or rec.get("source_sha") != kernel_source_sha(src_file):
+        return None
+    return rec["bytes_per_launch"]
+
+
+# ---------------------------------------------------------------------------
+# the GPU step
+# ---------------------------------------------------------------------------
+
+class Step:
+    """Preallocated buffers and the sequence of ABI calls of one step."""
+
+    STAGE_SRC = {"pool": "pool.hip", "route": "route.hip", "topk": "topk.hip", "gather": "gather.hip",
+                 "attn": "attn_prefill.hip"}
+
+    def __init__(self, cfg, workload, seed, dev):
+        import torch
+        import msa_inputs as mi
+        import routed_sparse_attention_msa_amd as msa
+        self.torch, self.msa, self.cfg, self.workload = torch, msa, cfg, workload
+        t = mi.draw_layer(cfg if workload == "prefill" else mi.PREFILL, seed=seed, device=dev)
+        if workload == "decode":
+            d = mi.draw_layer(cfg, seed=seed + 1, device=dev, with_raw=False)
+            for k in ("q", "k_loc", "v_loc", "q_r"):
+                t[k] = d[k]
+        self.t = t
+        cpd = cfg.chunks_per_doc
+        e = lambda *shape, dt=torch.bfloat16: torch.empty(shape, dtype=dt, device=dev)
+        self.kbar = e(cfg.n_chunks, cfg.heads_kv, cfg.dim)
+        self.vbar = e(cfg.n_chunks, cfg.heads_kv, cfg.dim)
+        self.kbar_r = e(cfg.n_chunks, cfg.heads_kv, cfg.dim)
+        self.knorm = e(cfg.n_chunks, cfg.heads_kv, dt=torch.float32)
+        self._pool()
+        if "q_r" not in t:
+            t["q_r"] = mi.plant_router_queries(self.kbar_r, t["planted"], t["q_r_noise"], cfg)
+        self.scores = e(cfg.batch, cfg.n_doc, dt=torch.float32)
+        self.ids = e(cfg.batch, cfg.topk, dt=torch.int32)
+        self.top = e(cfg.batch, cfg.topk, dt=torch.float32)
+        self.k_sel = e(cfg.batch, cfg.mem_len, cfg.heads_kv, cfg.dim)
+        self.v_sel = e(cfg.batch, cfg.mem_len, cfg.heads_kv, cfg.dim)
+        self.out = torch.empty_like(t["q"])
+        self.lse = e(cfg.batch, cfg.heads_q, cfg.q_len, dt=torch.float32)
+        u8 = lambda n: torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+        self.ws_route = u8(msa.msa_route_scores_workspace(cfg.batch, cfg.q_len, cfg.heads_kv, cfg.dim,
+                                                          cfg.n_doc, cpd, torch.bfloat16))
+        self.ws_topk = u8(msa.msa_topk_docs_workspace(cfg.batch, cfg.n_doc, cfg.topk))
+        self.ws_attn = u8(msa.msa_sparse_attn_workspace(cfg.batch, cfg.q_len, cfg.heads_q, cfg.heads_kv,
+                                                        cfg.dim, cfg.mem_len, cfg.loc_len, torch.bfloat16))
+        torch.cuda.synchronize()
+
+    def _pool(self):
+        c = self.cfg.chunk
+        self.msa.msa_pool_chunks(self.t["k"], c, xbar=self.kbar)
+        self.msa.msa_pool_chunks(self.t["v"], c, xbar=self.vbar)
+        self.msa.msa_pool_chunks(self.t["k_r"], c, xbar=self.kbar_r, xbar_norm=self.knorm)
+
+    def calls(self):
+        """(stage, callable) in step order."""
+        msa, t, cfg, c = self.msa, self.t, self.cfg, self.cfg.chunk
+        seq = []
+        if self.workload == "prefill":
+            seq += [("pool", lambda: msa.msa_pool_chunks(t["k"], c, xbar=self.kbar)),
+                    ("pool", lambda: msa.msa_pool_chunks(t["v"], c, xbar=self.vbar)),
+                    ("pool", lambda: msa.msa_pool_chunks(t["k_r"], c, xbar=self.kbar_r, xbar_norm=self.knorm))]
+        seq += [
+            ("route", lambda: msa.msa_route_scores(t["q_r"], self.kbar_r, self.knorm, cfg.chunks_per_doc,
+                                                   doc_scores=self.scores, ws=self.ws_route)),
+            ("topk", lambda: msa.msa_topk_docs(self.scores, cfg.topk, topk_ids=self.ids, topk_scores=self.top,
+                                               ws=self.ws_topk)),
+            ("gather", lambda: msa.msa_gather_kv(self.kbar, self.vbar, self.ids, cfg.chunks_per_doc,
+                                                 k_sel=self.k_sel, v_sel=self.v_sel)),
+            ("attn", lambda: msa.msa_sparse_attn(t["q"], self.k_sel, self.v_sel, t["k_loc"], t["v_loc"],
+                                                 out=self.out, lse=self.lse, ws=self.ws_attn)),
+        ]
+        return seq
+
+    def run(self, steps, events):
+        torch = self.torch
+        seq = self.calls()
+        marks = []
+        for _ in range(steps):
+            for stage, fn in seq:
+                if events:
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    fn()
+                    b.record()
+                    marks.append((stage, a, b))
+                else:
+                    fn()
+        return marks
+
+
+def cpu_baseline(step, cfg, workload):
+    """Time the float64 oracle on a bounded sample of the step and scale it up."""
+    import numpy as np
+    import torch
+    from oracle import pool_chunks_mean, route_scores, sparse_attention_rows, topk_docs
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    f = lambda x: x.detach().float().cpu().double().numpy()
+    rng = np.random.default_rng(0)
+    cpd = cfg.chunks_per_doc
+    secs = 0.0
+    parts = []
+    if workload == "prefill":
+        n_pool = 64
+        docs = torch.as_tensor(rng.choice(cfg.n_doc, n_pool, replace=False), device=step.t["k"].device)
+        for name in ("k", "v", "k_r"):
+            x = f(step.t[name][docs])
+            t0 = time.perf_counter()
+            pool_chunks_mean(x, cfg.chunk)
+            secs += (time.perf_counter() - t0) * cfg.n_doc / n_pool
+        parts.append(f"pool {n_pool}/{cfg.n_doc} docs x3 tensors")
+    n_route = 256
+    sample = rng.choice(cfg.n_doc, n_route, replace=False)
+    rows = torch.as_tensor((sample[:, None] * cpd + np.arange(cpd)).ravel(), device=step.kbar_r.device)
+    q_r, kb = f(step.t["q_r"]), f(step.kbar_r[rows])
+    t0 = time.perf_counter()
+    route_scores(q_r, kb, cpd)
+    secs += (time.perf_counter() - t0) * cfg.n_doc / n_route
+    parts.append(f"route all tokens vs {n_route}/{cfg.n_doc} docs")
+    sc = f(step.scores)
+    t0 = time.perf_counter()
+    topk_docs(sc, cfg.topk)
+    secs += time.perf_counter() - t0
+    parts.append("top-k whole")
+    # gather is a copy; attention on sampled rows (uniform over (b, t, h))
+    ks, vs = f(step.k_sel), f(step.v_sel)
+    kl, vl, q = f(step.t["k_loc"]), f(step.t["v_loc"]), f(step.t["q"])
+    n_rows_total = cfg.batch * cfg.q_len * cfg.heads_q
+    n_att = min(2048, n_rows_total)
+    g = cfg.heads_q // cfg.heads_kv
+    picks = rng.integers(0, n_rows_total, n_att)
+    t0 = time.perf_counter()
+    for r in picks:
+        h = int(r % cfg.heads_q)
+        tt = int((r // cfg.heads_q) % cfg.q_len)
+        b = int(r // (cfg.heads_q * cfg.q_len))
+        n_loc = cfg.loc_len - cfg.q_len + tt + 1
+        keys = np.concatenate([ks[b, :, h // g], kl[b, :n_loc, h // g]])
+        vals = np.concatenate([vs[b, :, h // g], vl[b, :n_loc, h // g]])
+        sparse_attention_rows(q[b, tt, h], keys, vals, 1.0 / math.sqrt(cfg.dim))
+    secs += (time.perf_counter() - t0) * n_rows_total / n_att
+    parts.append(f"attention {n_att}/{n_rows_total} rows")
+    tokens = cfg.batch * cfg.q_len
+    return {"value": tokens / secs, "unit": "query tokens/s", "cores": int(blas), "kind": "oracle",
+            "sample": "; ".join(parts) + "; each stage's time scaled to the full step",
+            "seconds_per_step_extrapolated": secs}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path; see DESIGN.md for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import msa_inputs as mi
+    dev = "cuda:0"
+    cfg = mi.PREFILL if args.workload == "prefill" else mi.DECODE
+    print(f"[bench] building inputs for {cfg.name}", file=sys.stderr, flush=True)
+    step = Step(cfg, args.workload, args.seed, dev)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    step.run(args.warmup, events=False)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, per-launch events inside
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    marks = step.run(args.steps, events=True)
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+
+    works = {"pool": None, "route": work_route(cfg), "topk": work_topk(cfg), "gather": work_gather(cfg),
+             "attn": work_attn(cfg)}
+    per = {}
+    counts = {}
+    for stage, a, b in marks:
+        per[stage] = per.get(stage, 0.0) + a.elapsed_time(b)
+        counts[stage] = counts.get(stage, 0) + 1
+    stages = {}
+    for stage in per:
+        n_launch = counts[stage]
+        avg = per[stage] / n_launch
+        w = works[stage] if stage != "pool" else work_pool(cfg, with_norm=False)
+        entry = roofline_entry(w, avg)
+        entry.update({"avg_launch_ms": avg, "launches_per_step": n_launch // args.steps,
+                      "ms_per_step": per[stage] / args.steps})
+        stages[stage] = entry
+    dom = max(stages, key=lambda s: stages[s]["ms_per_step"])
+    roof = {k: stages[dom][k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+    roof["kernel"] = dom
+    roof["avg_launch_ms"] = stages[dom]["avg_launch_ms"]
+    roof["traffic"] = measured_traffic(dom, Step.STAGE_SRC[dom], stages[dom]["launches_per_step"])
+
+    tokens = cfg.batch * cfg.q_len
+    online_ms = sum(stages[s]["ms_per_step"] for s in stages if s != "pool")
+    rec = {
+        "metric": "query tokens/s at 1M-token memory (routing-scan GB/s + sparse-attn TFLOP/s in stages)",
+        "value": tokens / (ms_per_step / 1e3),
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "n_docs": cfg.n_doc, "doc_len": cfg.doc_len, "chunk": cfg.chunk,
+                   "batch": cfg.batch, "q_len": cfg.q_len, "loc_len": cfg.loc_len, "heads_q": cfg.heads_q,
+                   "heads_kv": cfg.heads_kv, "dim": cfg.dim, "topk": cfg.topk,
+                   "step": ("pool K,V,K_r -> route -> top-k -> gather -> attention" if args.workload == "prefill"
+                            else "route -> top-k -> gather -> split-KV attention")},
+        "roofline": roof,
+        "stages": stages,
+        "online_tokens_per_s": tokens / (online_ms / 1e3),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(step, cfg, args.workload)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,31 +1,14 @@
-// Kernel selection for routing and attention: the bf16 MFMA kernels serve
+// Kernel selection for attention: the bf16 MFMA kernels serve
 // the shapes they are built for, the vector-ALU kernels serve every other
 // shape (float32, odd head dims).  Both are HIP; there is no CPU path.
 #include "internal.h"
 
 namespace msa {
 
-hipError_t launch_route_generic(const void* q_r, const void* kbar_r, const float* knorm, int batch,
-                                int q_len, int heads, int dim, int64_t n_docs, int cpd,
-                                msa_dtype dt, float* doc_scores, hipStream_t s);
 hipError_t launch_attn_generic(const void* q, const void* k_sel, const void* v_sel, int mem_len,
                                const void* k_loc, const void* v_loc, int loc_len, int batch,
                                int q_len, int heads_q, int heads_kv, int dim, float scale,
                                msa_dtype dt, void* out, float* lse, hipStream_t s);
-
-size_t route_workspace_bytes(int batch, int q_len, int heads, int dim, int64_t n_docs, int cpd,
-                             msa_dtype dt) {
-  (void)batch; (void)q_len; (void)heads; (void)dim; (void)n_docs; (void)cpd; (void)dt;
-  return 0;
-}
-
-hipError_t launch_route(const void* q_r, const void* kbar_r, const float* knorm, int batch,
-                        int q_len, int heads, int dim, int64_t n_docs, int cpd, msa_dtype dt,
-                        float* doc_scores, void* ws, hipStream_t s) {
-  (void)ws;
-  return launch_route_generic(q_r, kbar_r, knorm, batch, q_len, heads, dim, n_docs, cpd, dt,
-                              doc_scores, s);
-}
 
 size_t attn_workspace_bytes(int batch, int q_len, int heads_q, int heads_kv, int dim, int mem_len,
                             int loc_len, msa_dtype dt) {

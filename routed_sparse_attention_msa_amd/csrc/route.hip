@@ -1,0 +1,497 @@
+// S2: cosine routing scores on bf16 MFMA (gfx950, head dim 128).
+//
+// Method: MSA README (EverMind-AI/MSA), "Overall Design" -- each document is
+// scored by the cosine similarity of the query's router projection Q_r with
+// the pooled router keys, averaged over heads and maximised over the query
+// tokens; this implementation also maximises over the document's chunks.
+//
+//   score[b, doc] = max_{t, j} (1/H) sum_h <q[b,t,h], k[doc*C+j,h]> * iq[b,t,h] * ik[doc*C+j,h]
+//
+// with iq, ik the float32 inverse norms (max(norm, 1e-12)).  The raw dot
+// products run on bf16 MFMA: a product of two bf16 values is exact in
+// float32, and the normalised vectors are never rounded to bf16.
+//
+// Because every head carries its own (row, column) scale, the head sum is
+// not one long GEMM.  Per head the 32x32 MFMA accumulators are rescaled in
+// place ("chained" scaling): before head h the accumulator holds
+// sum_{h'<h} dot_h' * w_h' / w_{h-1} (w = iq * ik), is multiplied by
+// w_{h-1}/w_h, and after the last head by w_{H-1}/H.  This keeps a single
+// accumulator set per output tile; the per-head ratios come from small LDS
+// tables.
+//
+// MFMA operand k-order: within each 64-wide slice of a head, lane half hf
+// supplies the 32 contiguous elements [32*hf, 32*hf+32) in four 8-element
+// steps, so a lane reads 64 contiguous bytes per slice (16-byte loads).  A
+// (queries) and B (keys) use the same order, so each step still pairs
+// matching elements; only the float32 summation order changes.
+//
+// Two kernels:
+//  * route_stream  (few query rows): one workgroup owns 32 pooled chunks;
+//    each wave owns two heads, keeps their key fragments in registers
+//    (loaded straight from HBM with 16-byte loads, read exactly once), and
+//    loops over 32-row query tiles; the waves' head partials meet in LDS.
+//    HBM-bound: the bank streams once whatever the query count.
+//  * route_tiled   (many query rows): 256x256 output tile per workgroup,
+//    8 waves (2 x 4), each wave 128 rows x 64 columns (4 x 2 MFMA blocks);
+//    query and key slices are staged through XOR-swizzled, double-buffered
+//    LDS, 64 k-elements of one head per stage.  MFMA-bound.
+// Both end with the max over each document's chunks (cross-lane shuffles)
+// and over the query tokens of each sequence.
+#include "internal.h"
+
+namespace msa {
+namespace {
+
+constexpr float kEps = 1e-12f;
+constexpr int kDim = 128;  // head dim of the MFMA path
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Row of the 32x32 MFMA accumulator held in element i of lane-half hf.
+__device__ __forceinline__ int acc_row(int i, int hf) { return 8 * (i >> 2) + 4 * hf + (i & 3); }
+
+// ---------------------------------------------------------------------------
+// inverse query norms  iq[r][h] = 1 / max(|q_r[r,h]|, eps)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void route_qnorm_kernel(const uint16_t* __restrict__ q_r,
+                                                          int64_t rows, int heads,
+                                                          float* __restrict__ iq) {
+  // 16 lanes per (row, head): 16 lanes x 8 elements = 128.
+  const int64_t item = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+  const int sub = threadIdx.x & 15;
+  float ss = 0.f;
+  const bool ok = item < rows * heads;
+  if (ok) {
+    float f[8];
+    Vec16<uint16_t>::widen(load16(q_r + item * kDim + sub * 8), f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += f[i] * f[i];
+  }
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  if (ok && sub == 0) iq[item] = 1.f / fmaxf(sqrtf(ss), kEps);
+}
+
+// ---------------------------------------------------------------------------
+// epilogue helpers
+// ---------------------------------------------------------------------------
+
+// Max over the C consecutive columns (lanes) of each document.
+__device__ __forceinline__ float doc_max(float v, int cpd) {
+  for (int off = 1; off < cpd; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// stream kernel: T_tot small, any T with T | 32 or 32 | T
+// ---------------------------------------------------------------------------
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void route_stream_kernel(
+    const uint16_t* __restrict__ q_r, const uint16_t* __restrict__ kbar,
+    const float* __restrict__ knorm, int t_tot, int t_len, int heads, int64_t n_ch, int64_t n_docs,
+    int cpd, float* __restrict__ out) {
+  __shared__ float part[NW][16][64];
+  __shared__ float iq_s[NW][2][32];
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int cl = lane & 31, hf = lane >> 5;
+  const int64_t col = (int64_t)blockIdx.x * 32 + cl;
+  const bool col_ok = col < n_ch;
+  const size_t row_elems = (size_t)heads * kDim;
+
+  // Key fragments of this wave's two heads, straight from HBM (read once).
+  bf16x8 kf[2][8];
+  float ik[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int h = 2 * wave + j;
+    const bool ok = col_ok && h < heads;
+    const uint16_t* src = kbar + (ok ? (size_t)col * row_elems + (size_t)h * kDim : 0);
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        kf[j][4 * g + s] = as_bf16x8(ok ? load16(src + 64 * g + 32 * hf + 8 * s) : z);
+      }
+    ik[j] = ok ? 1.f / fmaxf(knorm[(size_t)col * heads + h], kEps) : 0.f;
+  }
+
+  const int n_tiles = (t_tot + 31) / 32;
+  const float inv_h = 1.f / (float)heads;
+  float run = -INFINITY;  // running max across row tiles of one sequence (T > 32)
+  for (int rt = 0; rt < n_tiles; ++rt) {
+    const int row0 = rt * 32;
+    const int row = row0 + cl;
+    float s[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int h = 2 * wave + j;
+      const bool ok = row < t_tot && h < heads;
+      const uint16_t* src = q_r + (ok ? (size_t)row * row_elems + (size_t)h * kDim : 0);
+      bf16x8 qf[8];
+      float ss = 0.f;
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          const u32x4 raw = ok ? load16(src + 64 * g + 32 * hf + 8 * st) : z;
+          float f[8];
+          Vec16<uint16_t>::widen(raw, f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+          qf[4 * g + st] = as_bf16x8(raw);
+        }
+      ss += __shfl_xor(ss, 32);
+      if (hf == 0) iq_s[wave][j][cl] = 1.f / fmaxf(sqrtf(ss), kEps);
+      f32x16 acc = {};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc = mfma32(qf[k], kf[j][k], acc);
+      __syncthreads();  // iq_s visible to every lane of the wave
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] += acc[i] * (iq_s[wave][j][acc_row(i, hf)] * ik[j]);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) part[wave][i][lane] = s[i];
+    __syncthreads();
+    if (wave == 0) {
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float tot = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) tot += part[w][i][lane];
+        v[i] = doc_max(tot * inv_h, cpd);
+      }
+      const bool writer = (cl % cpd) == 0 && col_ok;
+      const int64_t doc = col / cpd;
+      if (t_len >= 32) {
+        // the whole tile belongs to one sequence
+        float m = v[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) m = fmaxf(m, v[i]);
+        m = fmaxf(m, __shfl_xor(m, 32));
+        run = fmaxf(run, m);
+        if ((row0 + 32) % t_len == 0) {
+          const int b = row0 / t_len;
+          if (writer && hf == 0 && doc < n_docs) out[(size_t)b * n_docs + doc] = run;
+          run = -INFINITY;
+        }
+      } else if (t_len >= 8) {
+        // segments of t_len rows: groups of (t_len/8) register quads, both halves
+        const int quads = t_len >> 3;
+        for (int q0 = 0; q0 < 4; q0 += quads) {
+          float m = -INFINITY;
+          for (int q = q0; q < q0 + quads; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m = fmaxf(m, v[4 * q + e]);
+          m = fmaxf(m, __shfl_xor(m, 32));
+          const int r = row0 + 8 * q0;
+          if (writer && hf == 0 && r < t_tot && doc < n_docs) out[(size_t)(r / t_len) * n_docs + doc] = m;
+        }
+      } else {
+        // t_len in {1, 2, 4}: segments inside one register quad of one half
+        for (int i0 = 0; i0 < 16; i0 += t_len) {
+          float m = -INFINITY;
+          for (int e = 0; e < t_len; ++e) m = fmaxf(m, v[i0 + e]);
+          const int r = row0 + acc_row(i0, hf);
+          if (writer && r < t_tot && doc < n_docs) out[(size_t)(r / t_len) * n_docs + doc] = m;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// tiled kernel: many query rows, T % 32 == 0
+// ---------------------------------------------------------------------------
+constexpr int kTB = 256;             // rows per workgroup tile
+constexpr int kNB = 256;             // columns (pooled chunks) per workgroup tile
+constexpr int kTiledThreads = 512;   // 8 waves: 2 along rows x 4 along columns
+constexpr int kStageK = 64;          // k elements per LDS stage (half a head)
+constexpr int kMaxHeads = 8;         // scale tables sized for up to 8 heads (LDS budget)
+constexpr int kStreamMaxHeads = 16;
+
+struct TiledSmem {
+  uint8_t q[2][kTB * kStageK * 2];   // [buf][row][128 B], XOR-swizzled 16 B segments
+  uint8_t k[2][kNB * kStageK * 2];
+  float rq[kMaxHeads + 1][kTB];      // rq[h]: scale applied before head h (h = H: final)
+  float rk[kMaxHeads + 1][kNB];
+};
+
+__device__ __forceinline__ int swz(int row, int seg) { return row * 128 + ((seg ^ (row & 7)) << 4); }
+
+__global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
+    const uint16_t* __restrict__ q_r, const uint16_t* __restrict__ kbar,
+    const float* __restrict__ knorm, const float* __restrict__ iq, int t_tot, int t_len, int heads,
+    int64_t n_ch, int64_t n_docs, int cpd, int direct, float* __restrict__ partial,
+    float* __restrict__ out) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  TiledSmem& sm = *reinterpret_cast<TiledSmem*>(smem_raw);
+  float* red = reinterpret_cast<float*>(sm.q[0]);  // reused after the main loop: [8][kNB]
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int cl = lane & 31, hf = lane >> 5;
+  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves
+  const int row0 = blockIdx.y * kTB;
+  const int64_t col0 = (int64_t)blockIdx.x * kNB;
+  const size_t row_elems = (size_t)heads * kDim;
+
+  // --- per-head scale tables -------------------------------------------------
+  for (int idx = tid; idx < kTB; idx += kTiledThreads) {
+    const int r = row0 + idx;
+    float prev = 0.f;
+    for (int h = 0; h < heads; ++h) {
+      const float cur = r < t_tot ? iq[(size_t)r * heads + h] : 1.f;
+      if (h > 0) sm.rq[h][idx] = prev / cur;
+      prev = cur;
+    }
+    sm.rq[heads][idx] = prev;
+  }
+  for (int idx = tid; idx < kNB; idx += kTiledThreads) {
+    const int64_t n = col0 + idx;
+    float prev = 0.f;
+    for (int h = 0; h < heads; ++h) {
+      const float cur = n < n_ch ? 1.f / fmaxf(knorm[n * heads + h], kEps) : 0.f;
+      if (h > 0) sm.rk[h][idx] = cur != 0.f ? prev / cur : 0.f;
+      prev = cur;
+    }
+    sm.rk[heads][idx] = prev / (float)heads;
+  }
+
+  // --- staging: 4 x 16 B of q and 4 x 16 B of k per thread per stage ----------
+  u32x4 pq[4], pk[4];
+  auto gload = [&](int stage) {
+    const int h = stage >> 1, half = stage & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + kTiledThreads * i;
+      const int r = c >> 3, seg = c & 7;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      const int qr = row0 + r;
+      pq[i] = qr < t_tot ? load16(q_r + (size_t)qr * row_elems + h * kDim + half * 64 + seg * 8) : z;
+      const int64_t kn = col0 + r;
+      pk[i] = kn < n_ch ? load16(kbar + (size_t)kn * row_elems + h * kDim + half * 64 + seg * 8) : z;
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + kTiledThreads * i;
+      const int r = c >> 3, seg = c & 7;
+      *reinterpret_cast<u32x4*>(&sm.q[buf][swz(r, seg)]) = pq[i];
+      *reinterpret_cast<u32x4*>(&sm.k[buf][swz(r, seg)]) = pk[i];
+    }
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+
+  const int n_stages = 2 * heads;
+  gload(0);
+  lstore(0);
+  if (n_stages > 1) gload(1);
+  __syncthreads();
+
+  for (int st = 0; st < n_stages; ++st) {
+    const int buf = st & 1;
+    const uint8_t* qs = sm.q[buf];
+    const uint8_t* ks = sm.k[buf];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int seg = 4 * hf + s;
+      bf16x8 af[4], bfr[2];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int r = wm * 128 + a * 32 + cl;
+        af[a] = *reinterpret_cast<const bf16x8*>(qs + swz(r, seg));
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int r = wn * 64 + b * 32 + cl;
+        bfr[b] = *reinterpret_cast<const bf16x8*>(ks + swz(r, seg));
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = mfma32(af[a], bfr[b], acc[a][b]);
+    }
+    if (st + 1 < n_stages) lstore(buf ^ 1);
+    if (st + 2 < n_stages) gload(st + 2);
+    __syncthreads();
+    if (st & 1) {
+      // head h = st/2 finished: chain to head h+1, or apply the final scale
+      const int hn = (st >> 1) + 1;
+      float ck[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) ck[b] = sm.rk[hn][wn * 64 + b * 32 + cl];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 rq4 = *reinterpret_cast<const f32x4*>(&sm.rq[hn][wm * 128 + a * 32 + 8 * q + 4 * hf]);
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[a][b][4 * q + e] *= rq4[e] * ck[b];
+        }
+      }
+    }
+  }
+
+  // --- epilogue: max over each row block's 32 rows, then each doc's chunks ----
+  const int ndw = kNB / cpd;  // documents per workgroup tile
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float m = acc[a][b][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) m = fmaxf(m, acc[a][b][i]);
+      m = fmaxf(m, __shfl_xor(m, 32));
+      m = doc_max(m, cpd);
+      const int c = wn * 64 + b * 32 + cl;
+      if (hf == 0 && (cl % cpd) == 0) red[(wm * 4 + a) * ndw + c / cpd] = m;
+    }
+  }
+  __syncthreads();
+  const int n_blk = t_tot / 32;
+  for (int idx = tid; idx < 8 * ndw; idx += kTiledThreads) {
+    const int rb = idx / ndw, dw = idx - rb * ndw;
+    const int gblk = blockIdx.y * 8 + rb;
+    if (gblk >= n_blk) continue;
+    const int b = gblk * 32 / t_len;
+    const bool start = rb == 0 || ((gblk - 1) * 32 / t_len) != b;
+    if (!start) continue;
+    float m = red[rb * ndw + dw];
+    for (int r2 = rb + 1; r2 < 8 && blockIdx.y * 8 + r2 < n_blk && (blockIdx.y * 8 + r2) * 32 / t_len == b; ++r2)
+      m = fmaxf(m, red[r2 * ndw + dw]);
+    const int64_t doc = col0 / cpd + dw;
+    if (doc >= n_docs) continue;
+    if (direct)
+      out[(size_t)b * n_docs + doc] = m;
+    else
+      partial[(size_t)gblk * n_docs + doc] = m;
+  }
+}
+
+// out[b][doc] = max over the partial rows written for sequence b: its first
+// 32-row block and every block that starts a 256-row tile.
+__global__ __launch_bounds__(256) void route_combine_kernel(const float* __restrict__ partial,
+                                                            int t_len, int batch, int64_t n_docs,
+                                                            float* __restrict__ out) {
+  const int64_t doc = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int b = blockIdx.y;
+  if (doc >= n_docs) return;
+  const int blk0 = b * t_len / 32, blk1 = (b + 1) * t_len / 32;
+  float m = -INFINITY;
+  for (int g = blk0; g < blk1; ++g)
+    if (g == blk0 || (g % 8) == 0) m = fmaxf(m, partial[(size_t)g * n_docs + doc]);
+  out[(size_t)b * n_docs + doc] = m;
+}
+
+enum class RoutePath { Generic, Stream, Tiled };
+
+constexpr int kStreamMaxRows = 128;
+
+RoutePath pick(int batch, int q_len, int heads, int dim, int cpd, msa_dtype dt) {
+  if (dt != MSA_BF16 || dim != kDim || heads > kStreamMaxHeads) return RoutePath::Generic;
+  if (cpd > 32 || (32 % cpd) != 0) return RoutePath::Generic;
+  const int64_t t_tot = (int64_t)batch * q_len;
+  const bool small_t = q_len <= 32 && (32 % q_len) == 0;
+  const bool t32 = q_len % 32 == 0;
+  if (t_tot <= kStreamMaxRows && (small_t || t32)) return RoutePath::Stream;
+  if (t32 && heads <= kMaxHeads) return RoutePath::Tiled;
+  if (small_t) return RoutePath::Stream;
+  return RoutePath::Generic;
+}
+
+// direct: every sequence's rows lie inside one 256-row tile
+bool tiled_direct(int q_len) { return q_len <= kTB && (kTB % q_len) == 0; }
+
+}  // namespace
+
+hipError_t launch_route_generic(const void* q_r, const void* kbar_r, const float* knorm, int batch,
+                                int q_len, int heads, int dim, int64_t n_docs, int cpd,
+                                msa_dtype dt, float* doc_scores, hipStream_t s);
+
+size_t route_workspace_bytes(int batch, int q_len, int heads, int dim, int64_t n_docs, int cpd,
+                             msa_dtype dt) {
+  if (pick(batch, q_len, heads, dim, cpd, dt) != RoutePath::Tiled) return 0;
+  const size_t t_tot = (size_t)batch * q_len;
+  size_t bytes = t_tot * heads * sizeof(float);  // inverse query norms
+  bytes = (bytes + 255) & ~(size_t)255;
+  if (!tiled_direct(q_len)) bytes += (t_tot / 32) * (size_t)n_docs * sizeof(float);
+  return bytes;
+}
+
+hipError_t launch_route(const void* q_r, const void* kbar_r, const float* knorm, int batch,
+                        int q_len, int heads, int dim, int64_t n_docs, int cpd, msa_dtype dt,
+                        float* doc_scores, void* ws, hipStream_t s) {
+  const RoutePath path = pick(batch, q_len, heads, dim, cpd, dt);
+  const int64_t n_ch = n_docs * cpd;
+  const int t_tot = batch * q_len;
+  const uint16_t* q = static_cast<const uint16_t*>(q_r);
+  const uint16_t* k = static_cast<const uint16_t*>(kbar_r);
+  if (path == RoutePath::Generic)
+    return launch_route_generic(q_r, kbar_r, knorm, batch, q_len, heads, dim, n_docs, cpd, dt,
+                                doc_scores, s);
+  if (path == RoutePath::Stream) {
+    const unsigned grid = (unsigned)((n_ch + 31) / 32);
+    const int nw = (heads + 1) / 2;
+#define MSA_STREAM(NW)                                                                         \
+  case NW:                                                                                     \
+    hipLaunchKernelGGL(route_stream_kernel<NW>, dim3(grid), dim3(NW * 64), 0, s, q, k, knorm, \
+                       t_tot, q_len, heads, n_ch, n_docs, cpd, doc_scores);                    \
+    break;
+    switch (nw) {
+      MSA_STREAM(1)
+      MSA_STREAM(2)
+      MSA_STREAM(3)
+      MSA_STREAM(4)
+      MSA_STREAM(5)
+      MSA_STREAM(6)
+      MSA_STREAM(7)
+      MSA_STREAM(8)
+      default:
+        return hipErrorInvalidValue;
+    }
+#undef MSA_STREAM
+    return hipGetLastError();
+  }
+  // tiled
+  float* iq = static_cast<float*>(ws);
+  size_t off = ((size_t)t_tot * heads * sizeof(float) + 255) & ~(size_t)255;
+  float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + off);
+  const int64_t items = (int64_t)t_tot * heads;
+  hipLaunchKernelGGL(route_qnorm_kernel, dim3((unsigned)((items * 16 + 255) / 256)), dim3(256), 0, s,
+                     q, (int64_t)t_tot, heads, iq);
+  const bool direct = tiled_direct(q_len);
+  dim3 grid((unsigned)((n_ch + kNB - 1) / kNB), (unsigned)((t_tot + kTB - 1) / kTB));
+  const size_t smem = sizeof(TiledSmem);
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(route_tiled_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)smem);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(route_tiled_kernel, grid, dim3(kTiledThreads), smem, s, q, k, knorm, iq, t_tot,
+                     q_len, heads, n_ch, n_docs, cpd, direct ? 1 : 0, partial, doc_scores);
+  if (!direct) {
+    hipLaunchKernelGGL(route_combine_kernel, dim3((unsigned)((n_docs + 255) / 256), batch), dim3(256),
+                       0, s, partial, q_len, batch, n_docs, doc_scores);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -88,6 +88,20 @@ def _route_case(batch, q_len, heads, dim, n_docs, cpd, dtype, seed, planted=None
     (1, 33, 8, 128, 40, 8, torch.bfloat16),       # odd query length
     (2, 16, 4, 64, 50, 4, torch.bfloat16),        # other head count / dim / chunks
     (1, 8, 3, 96, 20, 5, torch.bfloat16),         # shape-general path
+    # MFMA tiled path: direct and combined partials, ragged column tiles
+    (1, 512, 8, 128, 100, 8, torch.bfloat16),     # 2 row tiles per sequence, combine
+    (3, 96, 8, 128, 70, 8, torch.bfloat16),       # sequences straddle 256-row tiles
+    (5, 64, 8, 128, 33, 8, torch.bfloat16),       # several sequences per tile, direct
+    (1, 2048, 8, 128, 300, 8, torch.bfloat16),    # prefill query length
+    (1, 512, 8, 128, 64, 16, torch.bfloat16),     # 16 chunks per document
+    (1, 256, 4, 128, 90, 8, torch.bfloat16),      # 4 heads
+    (1, 256, 1, 128, 64, 2, torch.bfloat16),      # 1 head
+    # MFMA stream path: odd head counts, 16 heads, one chunk per document
+    (2, 32, 5, 128, 50, 8, torch.bfloat16),
+    (1, 8, 16, 128, 40, 8, torch.bfloat16),
+    (2, 2, 8, 128, 200, 1, torch.bfloat16),
+    (32, 1, 8, 128, 2048, 8, torch.bfloat16),     # decode: 32 sequences x 1 token
+    (2, 16, 8, 128, 100, 32, torch.bfloat16),     # 32 chunks per document
 ])
 def test_route_parity(batch, q_len, heads, dim, n_docs, cpd, dtype):
     case(f"route B={batch} T={q_len} H={heads} d={dim} N={n_docs} C={cpd} {dtype}")
