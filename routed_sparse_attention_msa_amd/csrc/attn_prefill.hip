@@ -15,9 +15,17 @@
 // half adds one xor-32 shuffle), the O^T rescale is a scalar multiply, and the
 // P^T operand of the second product is the lane's own S^T values converted to
 // bf16 -- no cross-lane traffic.  The key order inside each 32-key block is
-// chosen so that holds; V is staged in LDS as interleaved key pairs (one
-// 32-bit word = the same d of two consecutive keys), so each V^T operand is
-// four 32-bit LDS reads.
+// chosen so that holds, and V is staged in LDS already in V^T operand order
+// (one 16-byte unit = the 8 keys one lane contributes to one MFMA, at one d),
+// so each V^T operand is a single 16-byte LDS read.  K tiles are stored in
+// an XOR-swizzled layout that keeps the operand reads free of bank
+// conflicts.  Each MFMA group's operand reads are issued before the group
+// (one LDS latency per group, not per MFMA).  K and V rows are fetched with
+// buffer loads: a per-lane byte offset fixed for the whole kernel plus a
+// per-tile scalar offset, so no address arithmetic runs per load except on
+// the last tile and on a tile that straddles the memory/local boundary.  The
+// softmax scale is folded into one FMA before exp2, and probabilities are
+// packed to bf16 by the hardware converter.
 //
 // Work split: one workgroup = (sequence, KV head, 32-token block); its waves
 // are the query heads of that KV group (GQA packing: each K/V tile is staged
@@ -25,21 +33,25 @@
 // the next tile's global loads in flight during the current tile's math.
 // Keys are a virtual sequence [memory rows ; local rows]; blocks fully below
 // every query's causal limit skip the mask, blocks beyond the last query's
-// limit are never loaded.  Workgroups are issued longest-first.
+// limit are never loaded.  When the whole grid is resident at once (two
+// workgroups per CU) the blocks are ordered so that the k-th and the
+// (k + grid/2)-th workgroup -- which share a CU -- hold mirrored token blocks
+// and equal work; otherwise the longest blocks go first.
 #include "internal.h"
 
 namespace msa {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kKT = 64;          // keys per LDS tile
-constexpr int kVStride = 144;    // 32-bit words per key-pair row of the V tile (128 + pad)
+constexpr int kKT = 64;                 // keys per LDS tile
+constexpr int kVGStride = 144;          // 16 B units per V group row: 128 d + one pad unit per 8
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 struct PrefillSmem {
-  uint8_t k[2][kKT * kD * 2];             // [key][256 B], XOR-swizzled 16 B segments
-  uint32_t v[2][(kKT / 2) * kVStride];    // [key pair][d]: V[2p][d] | V[2p+1][d] << 16
+  uint8_t k[2][kKT * 256];                // [key][256 B], 16 B segments XOR (key & 15)
+  uint8_t v[2][8 * kVGStride * 16];       // [group][d + d/8][8 bf16]
 };
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
@@ -47,33 +59,49 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 }
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ int acc_row(int i, int hf) { return 8 * (i >> 2) + 4 * hf + (i & 3); }
-__device__ __forceinline__ int kswz(int key, int seg) { return key * 256 + ((seg ^ (key & 7)) << 4); }
+__device__ __forceinline__ int kswz(int key, int seg) { return key * 256 + ((seg ^ (key & 15)) << 4); }
+// V group G = 4*kb + 2*s2 + hf holds keys 32kb + 16s2 + 4hf + {0..3, 8..11} of the tile.
+__device__ __forceinline__ int vunit(int grp, int d) { return (grp * kVGStride + d + (d >> 3)) * 16; }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ uint32_t perm_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
-// Two bf16 of one key and two of the next key -> the (key pair) words for two d's.
-__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
-__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
-
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const bf16x2v v = {(__bf16)lo, (__bf16)hi};   // v_cvt_pk_bf16_f32, round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
 }
 
-struct KeySrc {
-  const uint16_t* sel;
-  const uint16_t* loc;
-  int mem_len, loc_len, heads_kv, b, g;
-  __device__ __forceinline__ const uint16_t* row(int kappa) const {
-    if (kappa < mem_len) return sel + (((size_t)b * mem_len + kappa) * heads_kv + g) * kD;
-    return loc + (((size_t)b * loc_len + (kappa - mem_len)) * heads_kv + g) * kD;
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Rows of the virtual key sequence [memory rows ; local rows] of one (sequence, KV head).
+struct KVRows {
+  __amdgpu_buffer_rsrc_t sel, loc;   // based at the sequence's first row, sized to its rows
+  int mem_len;
+  uint32_t rs;                       // row stride in bytes (heads_kv * 256)
+  // 16 bytes at byte `in_row` of key row kappa0 + r.  Fast path: the whole tile lies
+  // inside memory or inside local rows and below `kend`, and `voff` = r*rs + in_row.
+  __device__ __forceinline__ u32x4 fast(int kappa0, uint32_t voff) const {
+    if (kappa0 >= mem_len) return bload(loc, voff, (uint32_t)(kappa0 - mem_len) * rs);
+    return bload(sel, voff, (uint32_t)kappa0 * rs);
+  }
+  // Any tile: clamp past `kend`, choose memory or local per row.
+  __device__ __forceinline__ u32x4 slow(int kappa0, int r, uint32_t in_row, int kend) const {
+    const int kappa = min(kappa0 + r, kend - 1);
+    const u32x4 a = bload(sel, (uint32_t)min(kappa, max(mem_len - 1, 0)) * rs + in_row, 0);
+    const u32x4 b = bload(loc, (uint32_t)max(kappa - mem_len, 0) * rs + in_row, 0);
+    return kappa < mem_len ? a : b;
   }
 };
 
 template <int NW>
-__global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_sel,
     const uint16_t* __restrict__ v_sel, int mem_len, const uint16_t* __restrict__ k_loc,
     const uint16_t* __restrict__ v_loc, int loc_len, int batch, int q_len, int heads_q, int heads_kv,
-    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    float scale_log2, int mirror, uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int kThreads = NW * 64;
   extern __shared__ __align__(16) uint8_t smem_raw[];
   PrefillSmem& sm = *reinterpret_cast<PrefillSmem*>(smem_raw);
@@ -85,20 +113,33 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(
   const int hsub = group / NW;                  // head sub-groups per KV head
   const int n_tblk = (q_len + 31) / 32;
 
-  // blockIdx -> (token block, sequence, kv head, head sub-group); longest first
+  // blockIdx -> (token block, sequence, kv head, head sub-group)
   int bid = blockIdx.x;
   const int hs = bid % hsub;
   bid /= hsub;
   const int g = bid % heads_kv;
   bid /= heads_kv;
   const int b = bid % batch;
-  const int tb = n_tblk - 1 - bid / batch;
+  const int idx = bid / batch;
+  const int upper = (n_tblk + 1) / 2;
+  const int tb = !mirror ? n_tblk - 1 - idx : (idx < upper ? n_tblk - 1 - idx : idx - upper);
   const int h = g * group + hs * NW + wave;
   const int t0 = tb * 32;
   const int t = t0 + cl;                        // this lane's query token
   const bool t_ok = t < q_len;
 
-  const KeySrc ks{k_sel, k_loc, mem_len, loc_len, heads_kv, b, g};
+  const uint32_t rs = (uint32_t)heads_kv * kD * 2;
+  const size_t sel_rows = (size_t)b * mem_len * heads_kv * kD;
+  const size_t loc_rows = (size_t)b * loc_len * heads_kv * kD;
+  const uint32_t sel_bytes = (uint32_t)((size_t)mem_len * rs);
+  const uint32_t loc_bytes = (uint32_t)((size_t)loc_len * rs);
+  const KVRows kr{__builtin_amdgcn_make_buffer_rsrc((void*)(k_sel + (mem_len ? sel_rows : 0)), (short)0, sel_bytes, kRsrcWord3),
+                  __builtin_amdgcn_make_buffer_rsrc((void*)(k_loc + loc_rows), (short)0, loc_bytes, kRsrcWord3),
+                  mem_len, rs};
+  const KVRows vr{__builtin_amdgcn_make_buffer_rsrc((void*)(v_sel + (mem_len ? sel_rows : 0)), (short)0, sel_bytes, kRsrcWord3),
+                  __builtin_amdgcn_make_buffer_rsrc((void*)(v_loc + loc_rows), (short)0, loc_bytes, kRsrcWord3),
+                  mem_len, rs};
+
   const int causal0 = mem_len + loc_len - q_len;          // token t sees kappa < causal0 + t + 1
   const int kend = causal0 + min(t0 + 32, q_len);          // keys needed by the block
   const int n_tiles = (kend + kKT - 1) / kKT;
@@ -115,67 +156,78 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(
     }
   }
 
-  // staging: K 64 rows x 16 segments; V 32 key pairs x 16 segments (two rows each)
+  // Staging assignments (fixed for the kernel).
+  //  K: chunk c = tid + kThreads*i -> key row c/16 = tid/16 + (kThreads/16)*i, 16 B segment
+  //     tid%16 (coalesced rows); one lane byte offset, the row term goes to the scalar offset.
+  //  V: task  c = tid + kThreads*i -> group c/32, half (c/16)%2, d-block c%16: four key rows
+  //     of 8 d each, rewritten as 8 half-units (4 keys at one d) of that group.
   constexpr int kKChunks = kKT * 16 / kThreads;
-  constexpr int kVChunks = (kKT / 2) * 16 / kThreads;
-  u32x4 pk[kKChunks], pv0[kVChunks], pv1[kVChunks];
+  constexpr int kKRowStep = kThreads / 16;
+  constexpr int kVTasks = 256 / kThreads;
+  const uint32_t goff = (uint32_t)g * kD * 2;
+  const int krow0 = tid >> 4;
+  const uint32_t k_in_row = goff + (tid & 15) * 16;
+  const uint32_t kvoff = (uint32_t)krow0 * rs + k_in_row;
+  auto vtask_row0 = [&](int i) {
+    const int c = tid + kThreads * i;
+    const int grp = c >> 5, half = (c >> 4) & 1;
+    return 32 * (grp >> 2) + 16 * ((grp >> 1) & 1) + 4 * (grp & 1) + 8 * half;
+  };
+  const uint32_t v_in_row = goff + (tid & 15) * 16;   // d-block = c % 16 = tid % 16
+  u32x4 pk[kKChunks], pv[kVTasks][4];
   auto gload = [&](int tile) {
     const int kappa0 = tile * kKT;
+    const bool fast = kappa0 + kKT <= kend && (kappa0 >= mem_len || kappa0 + kKT <= mem_len);
+    if (fast) {
 #pragma unroll
-    for (int i = 0; i < kKChunks; ++i) {
-      const int c = tid + kThreads * i;
-      const int r = c >> 4, seg = c & 15;
-      const int kappa = kappa0 + r;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      pk[i] = kappa < kend ? load16(ks.row(kappa) + seg * 8) : z;
-    }
+      for (int i = 0; i < kKChunks; ++i) pk[i] = kr.fast(kappa0 + kKRowStep * i, kvoff);
 #pragma unroll
-    for (int i = 0; i < kVChunks; ++i) {
-      const int c = tid + kThreads * i;
-      const int p = c >> 4, seg = c & 15;
-      const int k0 = kappa0 + 2 * p;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      const KeySrc vs{v_sel, v_loc, mem_len, loc_len, heads_kv, b, g};
-      pv0[i] = k0 < kend ? load16(vs.row(k0) + seg * 8) : z;
-      pv1[i] = k0 + 1 < kend ? load16(vs.row(k0 + 1) + seg * 8) : z;
+      for (int i = 0; i < kVTasks; ++i) {
+        const uint32_t voff = (uint32_t)vtask_row0(i) * rs + v_in_row;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pv[i][j] = vr.fast(kappa0 + j, voff);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kKChunks; ++i) pk[i] = kr.slow(kappa0, krow0 + kKRowStep * i, k_in_row, kend);
+#pragma unroll
+      for (int i = 0; i < kVTasks; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pv[i][j] = vr.slow(kappa0, vtask_row0(i) + j, v_in_row, kend);
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < kKChunks; ++i) {
       const int c = tid + kThreads * i;
-      const int r = c >> 4, seg = c & 15;
-      *reinterpret_cast<u32x4*>(&sm.k[buf][kswz(r, seg)]) = pk[i];
+      *reinterpret_cast<u32x4*>(&sm.k[buf][kswz(c >> 4, c & 15)]) = pk[i];
     }
 #pragma unroll
-    for (int i = 0; i < kVChunks; ++i) {
+    for (int i = 0; i < kVTasks; ++i) {
       const int c = tid + kThreads * i;
-      const int p = c >> 4, seg = c & 15;
-      const u32x4 a = pv0[i], bb = pv1[i];
-      u32x4 w0, w1;  // d = seg*8 + 0..3 and + 4..7
-      w0[0] = pair_lo(a[0], bb[0]);
-      w0[1] = pair_hi(a[0], bb[0]);
-      w0[2] = pair_lo(a[1], bb[1]);
-      w0[3] = pair_hi(a[1], bb[1]);
-      w1[0] = pair_lo(a[2], bb[2]);
-      w1[1] = pair_hi(a[2], bb[2]);
-      w1[2] = pair_lo(a[3], bb[3]);
-      w1[3] = pair_hi(a[3], bb[3]);
-      uint32_t* dst = &sm.v[buf][p * kVStride + seg * 8];
-      *reinterpret_cast<u32x4*>(dst) = w0;
-      *reinterpret_cast<u32x4*>(dst + 4) = w1;
+      const int grp = c >> 5, half = (c >> 4) & 1, dblk = c & 15;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {   // d = 8*dblk + 2e and + 2e + 1
+        uint2 lo, hi;
+        lo.x = perm_lo(pv[i][0][e], pv[i][1][e]);
+        lo.y = perm_lo(pv[i][2][e], pv[i][3][e]);
+        hi.x = perm_hi(pv[i][0][e], pv[i][1][e]);
+        hi.y = perm_hi(pv[i][2][e], pv[i][3][e]);
+        *reinterpret_cast<uint2*>(&sm.v[buf][vunit(grp, 8 * dblk + 2 * e) + 8 * half]) = lo;
+        *reinterpret_cast<uint2*>(&sm.v[buf][vunit(grp, 8 * dblk + 2 * e + 1) + 8 * half]) = hi;
+      }
     }
   };
 
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-  float m = -INFINITY, l = 0.f;  // running max (log2 domain) and this half's running sum
+  float m = -INFINITY, l = 0.f;  // running max of the raw scores and this half's running sum
 
   gload(0);
   lstore(0);
-  if (n_tiles > 1) gload(1);
   __syncthreads();
+  if (n_tiles > 1) gload(1);
 
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int buf = tile & 1;
@@ -184,31 +236,37 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
+      bf16x8 kf[8];
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         const int seg = 8 * (st >> 2) + 4 * hf + (st & 3);
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sm.k[buf][kswz(kb * 32 + cl, seg)]);
-        s[kb] = mfma32(kf, qf[st], s[kb]);
+        kf[st] = *reinterpret_cast<const bf16x8*>(&sm.k[buf][kswz(kb * 32 + cl, seg)]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int st = 0; st < 8; ++st) s[kb] = mfma32(kf[st], qf[st], s[kb]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // scale, mask, tile max
-    const bool full = kappa0 + kKT <= full_below;
-    const int lim = causal0 + t + 1;
-    float mt = -INFINITY;
+    // mask (only tiles that cross the causal limit), tile max of the raw scores
+    if (kappa0 + kKT > full_below) {
+      const int lim = causal0 + t + 1;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kappa0 + kb * 32 + acc_row(i, hf) >= lim) s[kb][i] = -INFINITY;
+    }
+    float mt = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float v = s[kb][i] * scale_log2;
-        if (!full && kappa0 + kb * 32 + acc_row(i, hf) >= lim) v = -INFINITY;
-        s[kb][i] = v;
-        mt = fmaxf(mt, v);
-      }
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kb][i]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float m_new = fmaxf(m, mt);
-    const float alpha = fast_exp2(m - m_new);
+    const float alpha = fast_exp2((m - m_new) * scale_log2);
     m = m_new;
+    const float off = -m_new * scale_log2;
     float lsum = 0.f;
     bf16x8 pf[2][2];
 #pragma unroll
@@ -218,8 +276,8 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(
         u32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(s[kb][8 * s2 + 2 * e] - m_new);
-          const float p1 = fast_exp2(s[kb][8 * s2 + 2 * e + 1] - m_new);
+          const float p0 = fast_exp2(fmaf(s[kb][8 * s2 + 2 * e], scale_log2, off));
+          const float p1 = fast_exp2(fmaf(s[kb][8 * s2 + 2 * e + 1], scale_log2, off));
           lsum += p0 + p1;
           w[e] = pack_bf16x2(p0, p1);
         }
@@ -232,27 +290,24 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
     }
-    // O^T += V^T P^T
+    // O^T += V^T P^T: lane (d, hf) reads its 8 keys of group 4kb + 2s2 + hf at column d.
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        const int p = kb * 16 + 8 * s2 + 2 * hf;
-        const uint32_t* vrow = &sm.v[buf][p * kVStride];
+        const int grp = 4 * kb + 2 * s2 + hf;
+        bf16x8 vf[4];
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int d = db * 32 + cl;
-          u32x4 w;
-          w[0] = vrow[d];
-          w[1] = vrow[kVStride + d];
-          w[2] = vrow[4 * kVStride + d];
-          w[3] = vrow[5 * kVStride + d];
-          o[db] = mfma32(as_bf16x8(w), pf[kb][s2], o[db]);
-        }
+        for (int db = 0; db < 4; ++db)
+          vf[db] = *reinterpret_cast<const bf16x8*>(&sm.v[buf][vunit(grp, db * 32 + cl)]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db] = mfma32(vf[db], pf[kb][s2], o[db]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     if (tile + 1 < n_tiles) lstore(buf ^ 1);
-    if (tile + 2 < n_tiles) gload(tile + 2);
     __syncthreads();
+    if (tile + 2 < n_tiles) gload(tile + 2);
   }
 
   const float l_tot = l + __shfl_xor(l, 32);
@@ -269,7 +324,14 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(
       w.y = pack_bf16x2(o[db][4 * qd + 2] * inv_l, o[db][4 * qd + 3] * inv_l);
       *reinterpret_cast<uint2*>(orow + d0) = w;
     }
-  if (lse != nullptr && hf == 0) lse[((size_t)b * heads_q + h) * q_len + t] = (m + __log2f(l_tot)) * kLn2;
+  if (lse != nullptr && hf == 0)
+    lse[((size_t)b * heads_q + h) * q_len + t] = (m * scale_log2 + __log2f(l_tot)) * kLn2;
+}
+
+template <typename K>
+hipError_t set_smem(K kern, size_t bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
 }  // namespace
@@ -290,21 +352,30 @@ hipError_t launch_attn_prefill(const void* q, const void* k_sel, const void* v_s
   const int n_tblk = (q_len + 31) / 32;
   const unsigned grid = (unsigned)(n_tblk * batch * heads_kv * (group / nw));
   const size_t smem = sizeof(PrefillSmem);
+  static const hipError_t attr = [&] {
+    hipError_t e = set_smem(attn_prefill_kernel<4>, smem);
+    if (e == hipSuccess) e = set_smem(attn_prefill_kernel<2>, smem);
+    if (e == hipSuccess) e = set_smem(attn_prefill_kernel<1>, smem);
+    return e;
+  }();
+  if (attr != hipSuccess) return attr;
+  int dev = 0, n_cu = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  // Mirrored order when the whole grid fits in one round of two workgroups per CU.
+  const int mirror = (int)grid <= 2 * n_cu ? 1 : 0;
   const float sl2 = scale * kLog2e;
-  auto args = [&](auto kern) {
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (attr != hipSuccess) return attr;
+  auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * nw), smem, s, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k_sel), static_cast<const uint16_t*>(v_sel),
                        mem_len, static_cast<const uint16_t*>(k_loc),
                        static_cast<const uint16_t*>(v_loc), loc_len, batch, q_len, heads_q, heads_kv,
-                       sl2, static_cast<uint16_t*>(out), lse);
+                       sl2, mirror, static_cast<uint16_t*>(out), lse);
     return hipGetLastError();
   };
-  if (nw == 4) return args(attn_prefill_kernel<4>);
-  if (nw == 2) return args(attn_prefill_kernel<2>);
-  return args(attn_prefill_kernel<1>);
+  if (nw == 4) return go(attn_prefill_kernel<4>);
+  if (nw == 2) return go(attn_prefill_kernel<2>);
+  return go(attn_prefill_kernel<1>);
 }
 
 }  // namespace msa
