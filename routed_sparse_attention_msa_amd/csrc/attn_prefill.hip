@@ -27,16 +27,16 @@
 // softmax scale is folded into one FMA before exp2, and probabilities are
 // packed to bf16 by the hardware converter.
 //
-// Work split: one workgroup = (sequence, KV head, 32-token block); its waves
+// Work split: one workgroup = (sequence, KV head, 32-token block).  Its waves
 // are the query heads of that KV group (GQA packing: each K/V tile is staged
-// once for all of them).  K/V tiles of 64 keys are double-buffered in LDS,
-// the next tile's global loads in flight during the current tile's math.
-// Keys are a virtual sequence [memory rows ; local rows]; blocks fully below
-// every query's causal limit skip the mask, blocks beyond the last query's
-// limit are never loaded.  When the whole grid is resident at once (two
-// workgroups per CU) the blocks are ordered so that the k-th and the
-// (k + grid/2)-th workgroup -- which share a CU -- hold mirrored token blocks
-// and equal work; otherwise the longest blocks go first.
+// once for all of them) times two key halves: one wave set takes the even
+// 64-key tiles, the other the odd ones, each with its own double-buffered
+// LDS tiles, and the two partial softmax states merge through LDS at the end.
+// Splitting the keys inside the workgroup halves the longest workgroup's
+// critical path, which bounds a causal prefill whose longest block needs
+// every key.  Keys are a virtual sequence [memory rows ; local rows]; tiles
+// fully below every query's causal limit skip the mask, tiles beyond the
+// last query's limit are never loaded.  Workgroups are issued longest-first.
 #include "internal.h"
 
 namespace msa {
@@ -96,18 +96,22 @@ struct KVRows {
   }
 };
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_kernel(
+template <int NW, int SPLIT>
+__global__ __launch_bounds__(NW * 64 * SPLIT, SPLIT == 1 && NW == 4 ? 2 : 1) void attn_prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_sel,
     const uint16_t* __restrict__ v_sel, int mem_len, const uint16_t* __restrict__ k_loc,
     const uint16_t* __restrict__ v_loc, int loc_len, int batch, int q_len, int heads_q, int heads_kv,
-    float scale_log2, int mirror, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  constexpr int kThreads = NW * 64;
+    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  constexpr int kThreads = NW * 64;       // threads of one key half
   extern __shared__ __align__(16) uint8_t smem_raw[];
-  PrefillSmem& sm = *reinterpret_cast<PrefillSmem*>(smem_raw);
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // wave index made provably uniform so tile offsets stay in scalar registers
+  const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int part = wave_all / NW;         // key half (SPLIT = 2): tiles part, part + 2, ...
+  const int wave = wave_all - part * NW;  // query head within the workgroup
+  PrefillSmem& sm = reinterpret_cast<PrefillSmem*>(smem_raw)[part];
+  const int tid = threadIdx.x - part * kThreads;
+  const int lane = tid & 63;
   const int cl = lane & 31, hf = lane >> 5;
   const int group = heads_q / heads_kv;
   const int hsub = group / NW;                  // head sub-groups per KV head
@@ -120,9 +124,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_kernel(
   const int g = bid % heads_kv;
   bid /= heads_kv;
   const int b = bid % batch;
-  const int idx = bid / batch;
-  const int upper = (n_tblk + 1) / 2;
-  const int tb = !mirror ? n_tblk - 1 - idx : (idx < upper ? n_tblk - 1 - idx : idx - upper);
+  const int tb = n_tblk - 1 - bid / batch;
   const int h = g * group + hs * NW + wave;
   const int t0 = tb * 32;
   const int t = t0 + cl;                        // this lane's query token
@@ -224,14 +226,19 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_kernel(
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
   float m = -INFINITY, l = 0.f;  // running max of the raw scores and this half's running sum
 
-  gload(0);
-  lstore(0);
+  if (part < n_tiles) {
+    gload(part);
+    lstore(0);
+  }
   __syncthreads();
-  if (n_tiles > 1) gload(1);
+  if (part + SPLIT < n_tiles) gload(part + SPLIT);
 
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int buf = tile & 1;
+  const int n_steps = (n_tiles + SPLIT - 1) / SPLIT;
+  for (int step = 0; step < n_steps; ++step) {
+    const int buf = step & 1;
+    const int tile = SPLIT * step + part;
     const int kappa0 = tile * kKT;
+    if (tile < n_tiles) {
     // S^T for the tile's two 32-key blocks
     f32x16 s[2];
 #pragma unroll
@@ -305,10 +312,39 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_kernel(
         for (int db = 0; db < 4; ++db) o[db] = mfma32(vf[db], pf[kb][s2], o[db]);
         __builtin_amdgcn_sched_barrier(0);
       }
-    if (tile + 1 < n_tiles) lstore(buf ^ 1);
+    }
+    if (tile + SPLIT < n_tiles) lstore(buf ^ 1);
     __syncthreads();
-    if (tile + 2 < n_tiles) gload(tile + 2);
+    if (tile + 2 * SPLIT < n_tiles) gload(tile + 2 * SPLIT);
   }
+
+  if constexpr (SPLIT == 2) {
+  // merge the odd-tile half into the even-tile half (same head, same lane)
+  float* mg = reinterpret_cast<float*>(smem_raw) + (size_t)wave * 66 * 64;
+  if (part == 1) {
+    mg[lane] = m;
+    mg[64 + lane] = l;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mg[(2 + db * 16 + i) * 64 + lane] = o[db][i];
+  }
+  __syncthreads();
+  if (part == 1) return;
+  {
+    const float m1 = mg[lane], l1 = mg[64 + lane];
+    const float mm = fmaxf(m, m1);
+    const float a0 = fast_exp2((m - mm) * scale_log2);
+    const float a1 = fast_exp2((m1 - mm) * scale_log2);
+    l = l * a0 + l1 * a1;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] = o[db][i] * a0 + mg[(2 + db * 16 + i) * 64 + lane] * a1;
+    m = mm;
+  }
+  }
+
 
   const float l_tot = l + __shfl_xor(l, 32);
   if (!t_ok) return;
@@ -328,12 +364,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_kernel(
     lse[((size_t)b * heads_q + h) * q_len + t] = (m * scale_log2 + __log2f(l_tot)) * kLn2;
 }
 
-template <typename K>
-hipError_t set_smem(K kern, size_t bytes) {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-}
-
 }  // namespace
 
 bool attn_prefill_supported(int q_len, int heads_q, int heads_kv, int dim, msa_dtype dt) {
@@ -351,31 +381,47 @@ hipError_t launch_attn_prefill(const void* q, const void* k_sel, const void* v_s
   const int nw = group % 4 == 0 ? 4 : group;
   const int n_tblk = (q_len + 31) / 32;
   const unsigned grid = (unsigned)(n_tblk * batch * heads_kv * (group / nw));
-  const size_t smem = sizeof(PrefillSmem);
-  static const hipError_t attr = [&] {
-    hipError_t e = set_smem(attn_prefill_kernel<4>, smem);
-    if (e == hipSuccess) e = set_smem(attn_prefill_kernel<2>, smem);
-    if (e == hipSuccess) e = set_smem(attn_prefill_kernel<1>, smem);
+  static const hipError_t attr = [] {
+    hipError_t e = hipSuccess;
+    auto set = [&](auto kern, size_t bytes) {
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    };
+    set(attn_prefill_kernel<4, 1>, sizeof(PrefillSmem));
+    set(attn_prefill_kernel<2, 1>, sizeof(PrefillSmem));
+    set(attn_prefill_kernel<1, 1>, sizeof(PrefillSmem));
+    set(attn_prefill_kernel<4, 2>, 2 * sizeof(PrefillSmem));
+    set(attn_prefill_kernel<2, 2>, 2 * sizeof(PrefillSmem));
+    set(attn_prefill_kernel<1, 2>, 2 * sizeof(PrefillSmem));
     return e;
   }();
   if (attr != hipSuccess) return attr;
+  // Split each workgroup's keys over two wave sets when the grid is a single
+  // round of workgroups (the longest block then bounds the kernel); with many
+  // rounds the longest-first order balances the CUs on its own.
   int dev = 0, n_cu = 256;
   if (hipGetDevice(&dev) == hipSuccess)
     (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-  // Mirrored order when the whole grid fits in one round of two workgroups per CU.
-  const int mirror = (int)grid <= 2 * n_cu ? 1 : 0;
+  const bool split = (int)grid <= 2 * n_cu;
   const float sl2 = scale * kLog2e;
-  auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * nw), smem, s, static_cast<const uint16_t*>(q),
+  auto go = [&](auto kern, int threads, size_t smem) {
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), smem, s, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k_sel), static_cast<const uint16_t*>(v_sel),
                        mem_len, static_cast<const uint16_t*>(k_loc),
                        static_cast<const uint16_t*>(v_loc), loc_len, batch, q_len, heads_q, heads_kv,
-                       sl2, mirror, static_cast<uint16_t*>(out), lse);
+                       sl2, static_cast<uint16_t*>(out), lse);
     return hipGetLastError();
   };
-  if (nw == 4) return go(attn_prefill_kernel<4>);
-  if (nw == 2) return go(attn_prefill_kernel<2>);
-  return go(attn_prefill_kernel<1>);
+  const size_t one = sizeof(PrefillSmem);
+  if (split) {
+    if (nw == 4) return go(attn_prefill_kernel<4, 2>, 512, 2 * one);
+    if (nw == 2) return go(attn_prefill_kernel<2, 2>, 256, 2 * one);
+    return go(attn_prefill_kernel<1, 2>, 128, 2 * one);
+  }
+  if (nw == 4) return go(attn_prefill_kernel<4, 1>, 256, one);
+  if (nw == 2) return go(attn_prefill_kernel<2, 1>, 128, one);
+  return go(attn_prefill_kernel<1, 1>, 64, one);
 }
 
 }  // namespace msa

@@ -57,12 +57,37 @@ def _check(q, ks, vs, kl, vl, rtol, lse_atol):
     (2, 3, 8, 2, 128, 64, 129, torch.bfloat16),        # short multi-token step
     (1, 16, 2, 1, 64, 16, 20, torch.bfloat16),         # head dim 64
     (1, 9, 2, 2, 96, 5, 9, torch.float32),             # odd head dim
+    (1, 64, 4, 2, 128, 32, 64, torch.bfloat16),        # group size 2
 ])
 def test_attn_parity(batch, q_len, hq, hkv, dim, mem, loc, dtype):
     case(f"attn B={batch} T={q_len} Hq={hq} Hkv={hkv} d={dim} M={mem} L={loc} {dtype}")
     q, ks, vs, kl, vl = _attn_inputs(batch, q_len, hq, hkv, dim, mem, loc, dtype, seed=q_len + loc + mem)
     rtol = ATTN_RTOL_BF16 if dtype == torch.bfloat16 else ATTN_RTOL_F32
     _check(q, ks, vs, kl, vl, rtol, lse_atol=2e-3 if dtype == torch.bfloat16 else 1e-5)
+
+
+def test_attn_many_workgroups_sampled():
+    """More workgroups than one round on the GPU (the unsplit prefill kernel);
+    sampled rows against the oracle one by one."""
+    from oracle import sparse_attention_rows
+    case("attn many workgroups (sampled)")
+    b_, t_, hq, hkv, d, mem, loc = 3, 1024, 32, 8, 128, 96, 1100
+    q, ks, vs, kl, vl = _attn_inputs(b_, t_, hq, hkv, d, mem, loc, torch.bfloat16, seed=9)
+    out, lse = msa.msa_sparse_attn(q, ks, vs, kl, vl)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    g = hq // hkv
+    fo, fl = to_f64(out), to_f64(lse)
+    qq, kks, vvs, kkl, vvl = to_f64(q), to_f64(ks), to_f64(vs), to_f64(kl), to_f64(vl)
+    picks = [(0, 0, 0), (b_ - 1, t_ - 1, hq - 1)] + [
+        (int(rng.integers(b_)), int(rng.integers(t_)), int(rng.integers(hq))) for _ in range(60)]
+    for bb, tt, h in picks:
+        n_loc = loc - t_ + tt + 1
+        keys = np.concatenate([kks[bb, :, h // g], kkl[bb, :n_loc, h // g]])
+        vals = np.concatenate([vvs[bb, :, h // g], vvl[bb, :n_loc, h // g]])
+        o, l_ = sparse_attention_rows(qq[bb, tt, h], keys, vals, 1.0 / math.sqrt(d))
+        assert row_rel_l2(fo[bb, tt, h], o) <= ATTN_RTOL_BF16
+        assert abs(fl[bb, h, tt] - l_) <= 2e-3
 
 
 def test_attn_constant_values_give_one():
