@@ -37,6 +37,8 @@
 //    LDS, 64 k-elements of one head per stage.  MFMA-bound.
 // Both end with the max over each document's chunks (cross-lane shuffles)
 // and over the query tokens of each sequence.
+#include <algorithm>
+
 #include "internal.h"
 
 namespace msa {
@@ -84,6 +86,224 @@ __global__ __launch_bounds__(256) void route_qnorm_kernel(const uint16_t* __rest
 __device__ __forceinline__ float doc_max(float v, int cpd) {
   for (int off = 1; off < cpd; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
   return v;
+}
+
+// The same with DPP lane permutes (no LDS round trip): xor 1 and xor 2 inside
+// quads, then the half-row mirror pairs the two quads of each 8-lane group and
+// the row mirror the two halves of each 16-lane row.  Documents start at
+// multiples of C inside a 32-column tile, so they align with these groups.
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+  const int x = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false);
+  return fmaxf(v, __int_as_float(x));
+}
+__device__ __forceinline__ float doc_max_dpp(float v, int cpd) {
+  if (cpd >= 2) v = dpp_max<0xB1>(v);     // quad_perm [1,0,3,2]
+  if (cpd >= 4) v = dpp_max<0x4E>(v);     // quad_perm [2,3,0,1]
+  if (cpd >= 8) v = dpp_max<0x141>(v);    // row_half_mirror
+  if (cpd >= 16) v = dpp_max<0x140>(v);   // row_mirror
+  if (cpd >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// scan kernel: T_tot <= 32 (one 32-row query tile), HBM streaming
+// ---------------------------------------------------------------------------
+// Persistent: each workgroup walks column tiles of 32 pooled chunks (all heads:
+// 32 x H x 256 B, 64 KiB at H = 8).  The next tile is prefetched into registers
+// with fully coalesced 16-byte loads (a wave instruction reads 1 KiB of one
+// chunk row) while the current tile is read from LDS, where rows sit with
+// their 16-byte segments XOR-swizzled by the row index so the MFMA operand
+// reads (one row per lane) are bank-conflict free.  Each wave owns two heads:
+// their query operands and inverse norms stay in registers for the whole
+// kernel, and the per-head partial sums of the waves meet in LDS.
+template <int H>
+__global__ __launch_bounds__(H * 32, 2) void route_scan_kernel(
+    const uint16_t* __restrict__ q_r, const uint16_t* __restrict__ kbar,
+    const float* __restrict__ knorm, int t_tot, int t_len, int64_t n_ch, int64_t n_docs, int cpd,
+    int n_tiles, float* __restrict__ out) {
+  constexpr int NW = H / 2;                  // waves; wave w owns heads 2w, 2w+1
+  constexpr int kThreads = NW * 64;
+  constexpr int kRowBytes = H * kDim * 2;    // one pooled chunk, all heads
+  constexpr int kSegs = kRowBytes / 16;      // 16-byte segments per chunk row
+  constexpr int kPerThread = 32 * kSegs / kThreads;   // = 16
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  uint8_t* ktile = smem_raw;                                           // [32][kRowBytes], swizzled
+  // partials of the quads a wave does not own: [NW][kSlots][64] (slot = rank among them)
+  constexpr int kSlots = NW == 1 ? 1 : 4 - 4 / NW;
+  f32x4* part = reinterpret_cast<f32x4*>(smem_raw + 32 * kRowBytes);
+  float* qmax = reinterpret_cast<float*>(part + NW * kSlots * 64);     // [4 quads][64]
+  float* iqp = qmax + 4 * 64;                                          // [H][2][16]
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int cl = lane & 31, hf = lane >> 5;
+  constexpr size_t kRowElems = (size_t)H * kDim;
+
+  // query operands of this wave's two heads (zero rows past t_tot); inverse
+  // norms go to LDS in accumulator-row order: iqp[h][hf][i] = iq(row acc_row(i, hf))
+  bf16x8 qf[2][8];
+  {
+    float* iq_row = reinterpret_cast<float*>(part);      // scratch [H][32] before the loop
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int h = 2 * wave + j;
+      const bool ok = cl < t_tot;
+      const uint16_t* src = q_r + (ok ? (size_t)cl * kRowElems + (size_t)h * kDim : 0);
+      float ss = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const u32x4 raw = ok ? load16(src + 64 * (k >> 2) + 32 * hf + 8 * (k & 3)) : z;
+        float f[8];
+        Vec16<uint16_t>::widen(raw, f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+        qf[j][k] = as_bf16x8(raw);
+      }
+      ss += __shfl_xor(ss, 32);
+      if (hf == 0) iq_row[h * 32 + cl] = 1.f / fmaxf(sqrtf(ss), kEps);
+    }
+    __syncthreads();
+    for (int idx = tid; idx < H * 32; idx += kThreads) {
+      const int h = idx >> 5, hh = (idx >> 4) & 1, i = idx & 15;
+      iqp[idx] = iq_row[h * 32 + acc_row(i, hh)];
+    }
+    __syncthreads();
+  }
+
+  // register prefetch of one tile: chunk c = tid + kThreads*i -> row c/kSegs, segment c%kSegs
+  u32x4 pf[kPerThread];
+  float pnorm[2];
+  auto prefetch = [&](int tile) {
+    const int64_t col0 = (int64_t)tile * 32;
+    // norms first: loads retire in order, and the inverse is only taken when the
+    // tile is consumed, so nothing here waits for the 64 KiB in flight
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = col0 + cl;
+      pnorm[j] = col < n_ch ? knorm[col * H + 2 * wave + j] : 0.f;
+    }
+    if (col0 + 32 <= n_ch) {
+#pragma unroll
+      for (int i = 0; i < kPerThread; ++i) {
+        const int c = tid + kThreads * i;
+        pf[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+            kbar + (size_t)(col0 + c / kSegs) * kRowElems + (c % kSegs) * 8));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPerThread; ++i) {
+        const int c = tid + kThreads * i;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        pf[i] = col0 + c / kSegs < n_ch ? load16(kbar + (size_t)(col0 + c / kSegs) * kRowElems + (c % kSegs) * 8) : z;
+      }
+    }
+  };
+  auto swz = [](int r, int sg) { return r * kRowBytes + ((sg ^ (r & 15)) << 4); };
+
+  const float inv_h = 1.f / (float)H;
+  int tile = blockIdx.x;
+  if (tile < n_tiles) prefetch(tile);
+  for (; tile < n_tiles; tile += gridDim.x) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int c = tid + kThreads * i;
+      *reinterpret_cast<u32x4*>(ktile + swz(c / kSegs, c % kSegs)) = pf[i];
+    }
+    const bool col_ok = (int64_t)tile * 32 + cl < n_ch;
+    const float ik0 = col_ok ? 1.f / fmaxf(pnorm[0], kEps) : 0.f;
+    const float ik1 = col_ok ? 1.f / fmaxf(pnorm[1], kEps) : 0.f;
+    // the registers are free again: start the next tile before the barrier
+    const int next = tile + gridDim.x;
+    if (next < n_tiles) prefetch(next);
+    __syncthreads();
+
+    float sacc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int h = 2 * wave + j;
+      f32x16 acc = {};
+#pragma unroll
+      for (int k0 = 0; k0 < 8; k0 += 4) {
+        bf16x8 kf[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int kk = k0 + k;
+          kf[k] = *reinterpret_cast<const bf16x8*>(ktile + swz(cl, h * 16 + 8 * (kk >> 2) + 4 * hf + (kk & 3)));
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc = mfma32(qf[j][k0 + k], kf[k], acc);
+      }
+      const float ik = j == 0 ? ik0 : ik1;
+      const float* iqh = iqp + (h * 2 + hf) * 16;
+#pragma unroll
+      for (int i = 0; i < 16; i += 4) {
+        const f32x4 iq4 = *reinterpret_cast<const f32x4*>(iqh + i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sacc[i + e] += acc[i + e] * (iq4[e] * ik);
+      }
+    }
+    // Head sum: every wave owns register quad(s) q = wave (mod NW), i.e. the query
+    // rows 8q + 4hf + 0..3, and adds the other waves' partials of that quad.
+    // slot of quad q among the quads not owned by wave w: q - (number of owned quads below q)
+    auto slot = [](int w, int q) { return q - (q + NW - 1 - w) / NW; };
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (q % NW != wave)
+        part[(wave * kSlots + slot(wave, q)) * 64 + lane] = f32x4{sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]};
+    __syncthreads();
+    const int64_t col = (int64_t)tile * 32 + cl;
+    const bool writer = (cl % cpd) == 0 && col < n_ch;
+    const int64_t doc = col / cpd;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (q % NW != wave || 8 * q >= t_tot) continue;
+      float v[4] = {sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]};
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        if (w == wave) continue;
+        const f32x4 pv = part[(w * kSlots + slot(w, q)) * 64 + lane];
+        v[0] += pv[0];
+        v[1] += pv[1];
+        v[2] += pv[2];
+        v[3] += pv[3];
+      }
+      // max over each sequence's rows, then over the document's chunks
+      if (t_len <= 4) {
+        for (int e0 = 0; e0 < 4; e0 += t_len) {
+          float m = v[e0];
+          for (int e = 1; e < t_len; ++e) m = fmaxf(m, v[e0 + e]);
+          m = doc_max_dpp(m, cpd) * inv_h;
+          const int r = 8 * q + 4 * hf + e0;
+          if (writer && r < t_tot && doc < n_docs) out[(size_t)(r / t_len) * n_docs + doc] = m;
+        }
+      } else {
+        float m = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        if (t_len == 8) {
+          m = doc_max_dpp(m, cpd) * inv_h;
+          if (writer && hf == 0 && doc < n_docs) out[(size_t)q * n_docs + doc] = m;
+        } else {
+          qmax[q * 64 + lane] = m;
+        }
+      }
+    }
+    if (t_len >= 16) {
+      // a sequence spans t_len / 8 quads: the owner of its first quad combines them
+      __syncthreads();
+      const int quads = t_len >> 3;
+      for (int q0 = 0; q0 < 4 && 8 * q0 < t_tot; q0 += quads) {
+        if (q0 % NW != wave) continue;
+        float m = qmax[q0 * 64 + lane];
+        for (int qq = q0 + 1; qq < q0 + quads; ++qq) m = fmaxf(m, qmax[qq * 64 + lane]);
+        m = doc_max_dpp(m, cpd) * inv_h;
+        if (writer && hf == 0 && doc < n_docs) out[(size_t)(8 * q0 / t_len) * n_docs + doc] = m;
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -402,7 +622,7 @@ __global__ __launch_bounds__(256) void route_combine_kernel(const float* __restr
   out[(size_t)b * n_docs + doc] = m;
 }
 
-enum class RoutePath { Generic, Stream, Tiled };
+enum class RoutePath { Generic, Scan, Stream, Tiled };
 
 constexpr int kStreamMaxRows = 128;
 
@@ -412,6 +632,7 @@ RoutePath pick(int batch, int q_len, int heads, int dim, int cpd, msa_dtype dt) 
   const int64_t t_tot = (int64_t)batch * q_len;
   const bool small_t = q_len <= 32 && (32 % q_len) == 0;
   const bool t32 = q_len % 32 == 0;
+  if (t_tot <= 32 && small_t && (heads == 2 || heads == 4 || heads == 8)) return RoutePath::Scan;
   if (t_tot <= kStreamMaxRows && (small_t || t32)) return RoutePath::Stream;
   if (t32 && heads <= kMaxHeads) return RoutePath::Tiled;
   if (small_t) return RoutePath::Stream;
@@ -448,6 +669,30 @@ hipError_t launch_route(const void* q_r, const void* kbar_r, const float* knorm,
   if (path == RoutePath::Generic)
     return launch_route_generic(q_r, kbar_r, knorm, batch, q_len, heads, dim, n_docs, cpd, dt,
                                 doc_scores, s);
+  if (path == RoutePath::Scan) {
+    const int n_tiles = (int)((n_ch + 31) / 32);
+    const int nw = heads / 2;
+    const int slots = nw == 1 ? 1 : 4 - 4 / nw;
+    const size_t smem = (size_t)32 * heads * kDim * 2 + (size_t)nw * slots * 64 * 16 + 4 * 64 * 4 +
+                        (size_t)heads * 32 * 4;
+    int dev = 0, n_cu = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+      (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    const unsigned grid = (unsigned)std::min<int64_t>(n_tiles, (int64_t)n_cu * 2);
+    auto go = [&](auto kern) {
+      static const hipError_t attr = hipFuncSetAttribute(
+          reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, 80 * 1024);
+      if (attr != hipSuccess) return attr;
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(heads * 32), smem, s, q, k, knorm, t_tot, q_len, n_ch,
+                         n_docs, cpd, n_tiles, doc_scores);
+      return hipGetLastError();
+    };
+    switch (heads) {
+      case 2: return go(route_scan_kernel<2>);
+      case 4: return go(route_scan_kernel<4>);
+      default: return go(route_scan_kernel<8>);
+    }
+  }
   if (path == RoutePath::Stream) {
     const unsigned grid = (unsigned)((n_ch + 31) / 32);
     const int nw = (heads + 1) / 2;
