@@ -400,10 +400,7 @@ hipError_t launch_attn_prefill(const void* q, const void* k_sel, const void* v_s
   // Split each workgroup's keys over two wave sets when the grid is a single
   // round of workgroups (the longest block then bounds the kernel); with many
   // rounds the longest-first order balances the CUs on its own.
-  int dev = 0, n_cu = 256;
-  if (hipGetDevice(&dev) == hipSuccess)
-    (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-  const bool split = (int)grid <= 2 * n_cu;
+  const bool split = (int)grid <= 2 * device_cu_count();
   const float sl2 = scale * kLog2e;
   auto go = [&](auto kern, int threads, size_t smem) {
     hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), smem, s, static_cast<const uint16_t*>(q),

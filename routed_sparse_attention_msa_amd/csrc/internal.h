@@ -77,6 +77,21 @@ template <> struct Vec16<uint16_t> {
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void store16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+// Streaming variants for data touched once (no reuse through L2 / MALL).
+__device__ __forceinline__ u32x4 load16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void store16_stream(void* p, const u32x4& v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
+// Compute units of the current device (256 on MI355X).
+inline int device_cu_count() {
+  int dev = 0, n_cu = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  return n_cu;
+}
 
 // ---------------------------------------------------------------------------
 // launchers (each returns hipGetLastError() of its launches)

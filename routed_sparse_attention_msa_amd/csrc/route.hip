@@ -675,9 +675,7 @@ hipError_t launch_route(const void* q_r, const void* kbar_r, const float* knorm,
     const int slots = nw == 1 ? 1 : 4 - 4 / nw;
     const size_t smem = (size_t)32 * heads * kDim * 2 + (size_t)nw * slots * 64 * 16 + 4 * 64 * 4 +
                         (size_t)heads * 32 * 4;
-    int dev = 0, n_cu = 256;
-    if (hipGetDevice(&dev) == hipSuccess)
-      (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    const int n_cu = device_cu_count();
     const unsigned grid = (unsigned)std::min<int64_t>(n_tiles, (int64_t)n_cu * 2);
     auto go = [&](auto kern) {
       static const hipError_t attr = hipFuncSetAttribute(

@@ -57,6 +57,38 @@ def test_pool_parity(shape, chunk, dtype):
     _check_pool(x, chunk)
 
 
+def test_pool_many_chunks_per_workgroup():
+    """Enough chunks that a workgroup pools several (rows staged in LDS), with
+    a last workgroup that holds fewer than the others."""
+    case("pool 1031 chunks, several per workgroup")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    x = torch.randn((1031, 64, 2, 64), generator=g, device=DEV).to(torch.bfloat16)
+    _check_pool(x, 64)
+
+
+@pytest.mark.parametrize("n_docs", [2048, 2047])
+def test_pool_full_bank_sampled(n_docs):
+    """The 1M-token bank (512 rows x 8 heads x 128 per document, bf16) in the
+    launch configuration of the benchmark; sampled chunks against the oracle."""
+    case(f"pool full bank n_docs={n_docs} (sampled)")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(n_docs)
+    x = (torch.randn((n_docs, 512, 8, 128), generator=g, device=DEV) / 11.3).to(torch.bfloat16)
+    xbar, norm = msa.msa_pool_chunks(x, 64, with_norm=True)
+    torch.cuda.synchronize()
+    n_ch = n_docs * 8
+    rng = np.random.default_rng(n_docs)
+    picks = np.unique(np.concatenate([[0, 31, 32, n_ch - 1], rng.integers(0, n_ch, 60)]))
+    rows = x.view(n_ch, 64, 8, 128)[torch.as_tensor(picks, device=DEV)]
+    exact = pool_chunks_mean(to_f64(rows), 64)
+    got = xbar[torch.as_tensor(picks, device=DEV)]
+    assert bf16_ulp_distance(got, exact).max() <= 1
+    np.testing.assert_allclose(to_f64(norm[torch.as_tensor(picks, device=DEV)]), chunk_norms(to_f64(got)),
+                               rtol=2e-6, atol=1e-30)
+    del x
+
+
 def test_pool_is_deterministic():
     case("pool determinism")
     x = torch.randn((32, 512, 8, 128), device=DEV).to(torch.bfloat16)
