@@ -107,67 +107,93 @@ __device__ __forceinline__ float doc_max_dpp(float v, int cpd) {
 }
 
 // ---------------------------------------------------------------------------
-// scan kernel: T_tot <= 32 (one 32-row query tile), HBM streaming
+// scan kernel: T_tot <= 128 (up to four 32-row query blocks), HBM streaming
 // ---------------------------------------------------------------------------
-// Persistent: each workgroup walks column tiles of 32 pooled chunks (all heads:
-// 32 x H x 256 B, 64 KiB at H = 8).  The next tile is prefetched into registers
-// with fully coalesced 16-byte loads (a wave instruction reads 1 KiB of one
-// chunk row) while the current tile is read from LDS, where rows sit with
-// their 16-byte segments XOR-swizzled by the row index so the MFMA operand
-// reads (one row per lane) are bank-conflict free.  Each wave owns two heads:
-// their query operands and inverse norms stay in registers for the whole
-// kernel, and the per-head partial sums of the waves meet in LDS.
-template <int H>
-__global__ __launch_bounds__(H * 32, 2) void route_scan_kernel(
+// Persistent: each workgroup walks a contiguous range of column tiles of 32
+// pooled chunks (all heads: 32 x H x 256 B, 64 KiB at H = 8).  The next tile
+// is prefetched into registers with fully coalesced 16-byte loads (a wave
+// instruction reads 1 KiB of one chunk row) while the current tile is read
+// from LDS, where rows are padded by
+// 16 bytes so the MFMA operand reads (one row per lane, 16 bytes each) fall
+// in distinct banks; every operand address is then one per-thread base plus
+// a constant offset, which keeps the address registers out of the way of the
+// query operands.
+//
+// The waves form G groups of H/2; in a group, wave hp owns heads 2hp, 2hp+1
+// for QW query blocks (the group's blocks), whose query operands stay in
+// registers for the whole kernel.  A wave reads each key fragment from LDS
+// once and feeds it to the MFMAs of all its query blocks.  Its two heads share
+// one accumulator by chained scaling (x w0/w1 between them, x w1 after), and
+// the head-pair partials of a group's waves meet in LDS.
+template <int H, int QW, int G, int TLC>
+__global__ __launch_bounds__(H / 2 * G * 64, (QW == 1 && G == 1) ? 2 : 1) void route_scan_kernel(
     const uint16_t* __restrict__ q_r, const uint16_t* __restrict__ kbar,
     const float* __restrict__ knorm, int t_tot, int t_len, int64_t n_ch, int64_t n_docs, int cpd,
     int n_tiles, float* __restrict__ out) {
-  constexpr int NW = H / 2;                  // waves; wave w owns heads 2w, 2w+1
+  constexpr int NWH = H / 2;                 // waves per group (one per head pair)
+  constexpr int NW = NWH * G;
+  constexpr int QB = QW * G;                 // 32-row query blocks
   constexpr int kThreads = NW * 64;
   constexpr int kRowBytes = H * kDim * 2;    // one pooled chunk, all heads
   constexpr int kSegs = kRowBytes / 16;      // 16-byte segments per chunk row
-  constexpr int kPerThread = 32 * kSegs / kThreads;   // = 16
+  constexpr int kRowStride = kRowBytes + 16; // LDS row pitch (padded)
+  constexpr int kPerThread = 32 * kSegs / kThreads;
+  static_assert(kThreads % kSegs == 0 || kSegs % kThreads == 0, "tile rows must split evenly");
+  constexpr int kQuads = 4 * QW;             // accumulator quads (4 rows x 2 halves) per wave
+  constexpr int kSlots = kQuads - kQuads / NWH;   // quads a wave hands to their owners
+  constexpr int kSlotsAlloc = kSlots > 0 ? kSlots : 1;
+  static_assert(4 % NWH == 0, "head pairs per group must divide 4");
+  // TLC: sequence length class, 0: t_len in {1, 2, 4}; 1: t_len == 8; 2: t_len >= 16
+  static_assert(TLC >= 0 && TLC <= 2, "bad sequence length class");
   extern __shared__ __align__(16) uint8_t smem_raw[];
-  uint8_t* ktile = smem_raw;                                           // [32][kRowBytes], swizzled
-  // partials of the quads a wave does not own: [NW][kSlots][64] (slot = rank among them)
-  constexpr int kSlots = NW == 1 ? 1 : 4 - 4 / NW;
-  f32x4* part = reinterpret_cast<f32x4*>(smem_raw + 32 * kRowBytes);
-  float* qmax = reinterpret_cast<float*>(part + NW * kSlots * 64);     // [4 quads][64]
-  float* iqp = qmax + 4 * 64;                                          // [H][2][16]
+  uint8_t* ktile = smem_raw;                                             // [32][kRowStride]
+  f32x4* part = reinterpret_cast<f32x4*>(smem_raw + 32 * kRowStride);   // [NW][kSlots][64]
+  float* qmax = reinterpret_cast<float*>(part + NW * kSlotsAlloc * 64);  // [QB * 4][64]
+  float* iqr = qmax + QB * 4 * 64;   // [QB][NWH][hf][ratio | last][16], accumulator-row order
+  // (then, with two query blocks per wave, the pending scores [NW][4 * kQuads / NWH][64])
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int hp = wave % NWH, grp = wave / NWH;
   const int cl = lane & 31, hf = lane >> 5;
   constexpr size_t kRowElems = (size_t)H * kDim;
 
-  // query operands of this wave's two heads (zero rows past t_tot); inverse
-  // norms go to LDS in accumulator-row order: iqp[h][hf][i] = iq(row acc_row(i, hf))
-  bf16x8 qf[2][8];
+  // query operands of this wave's heads and blocks (zero rows past t_tot);
+  // inverse norms go through LDS into the per-row tables iqr
+  bf16x8 qf[QW][2][8];
   {
-    float* iq_row = reinterpret_cast<float*>(part);      // scratch [H][32] before the loop
+    float* iq_row = reinterpret_cast<float*>(ktile);      // scratch [QB * 32][H] before the loop
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int h = 2 * wave + j;
-      const bool ok = cl < t_tot;
-      const uint16_t* src = q_r + (ok ? (size_t)cl * kRowElems + (size_t)h * kDim : 0);
-      float ss = 0.f;
+    for (int qw = 0; qw < QW; ++qw) {
+      const int row = (grp * QW + qw) * 32 + cl;
+      const bool ok = row < t_tot;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        const u32x4 raw = ok ? load16(src + 64 * (k >> 2) + 32 * hf + 8 * (k & 3)) : z;
-        float f[8];
-        Vec16<uint16_t>::widen(raw, f);
+      for (int j = 0; j < 2; ++j) {
+        const int h = 2 * hp + j;
+        const uint16_t* src = q_r + (ok ? (size_t)row * kRowElems + (size_t)h * kDim : 0);
+        float ss = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
-        qf[j][k] = as_bf16x8(raw);
+        for (int k = 0; k < 8; ++k) {
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          const u32x4 raw = ok ? load16(src + 64 * (k >> 2) + 32 * hf + 8 * (k & 3)) : z;
+          float f[8];
+          Vec16<uint16_t>::widen(raw, f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+          qf[qw][j][k] = as_bf16x8(raw);
+        }
+        ss += __shfl_xor(ss, 32);
+        if (hf == 0) iq_row[row * H + h] = 1.f / fmaxf(sqrtf(ss), kEps);
       }
-      ss += __shfl_xor(ss, 32);
-      if (hf == 0) iq_row[h * 32 + cl] = 1.f / fmaxf(sqrtf(ss), kEps);
     }
     __syncthreads();
-    for (int idx = tid; idx < H * 32; idx += kThreads) {
-      const int h = idx >> 5, hh = (idx >> 4) & 1, i = idx & 15;
-      iqp[idx] = iq_row[h * 32 + acc_row(i, hh)];
+    for (int idx = tid; idx < QB * NWH * 2 * 16; idx += kThreads) {
+      const int i = idx & 15, hh = (idx >> 4) & 1, php = (idx >> 5) % NWH, qb = (idx >> 5) / NWH;
+      const int row = qb * 32 + acc_row(i, hh);
+      const float iq0 = iq_row[row * H + 2 * php], iq1 = iq_row[row * H + 2 * php + 1];
+      float* dst = iqr + ((qb * NWH + php) * 2 + hh) * 32;
+      dst[i] = iq0 / iq1;
+      dst[16 + i] = iq1;
     }
     __syncthreads();
   }
@@ -182,128 +208,195 @@ __global__ __launch_bounds__(H * 32, 2) void route_scan_kernel(
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int64_t col = col0 + cl;
-      pnorm[j] = col < n_ch ? knorm[col * H + 2 * wave + j] : 0.f;
+      pnorm[j] = col < n_ch ? knorm[col * H + 2 * hp + j] : 0.f;
     }
-    if (col0 + 32 <= n_ch) {
+    // chunk-row-major tile: thread tid's i-th 16 bytes sit at (tid + kThreads*i)*16.
+    // The resource ends at the bank's end, so a ragged last tile reads zeros.
+    const int64_t left = (n_ch - col0) * (int64_t)kRowBytes;
+    const int n_rec = left < 32 * kRowBytes ? (int)left : 32 * kRowBytes;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(kbar + (size_t)col0 * kRowElems), 0, n_rec, 0x00020000);
 #pragma unroll
-      for (int i = 0; i < kPerThread; ++i) {
-        const int c = tid + kThreads * i;
-        pf[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-            kbar + (size_t)(col0 + c / kSegs) * kRowElems + (c % kSegs) * 8));
-      }
-    } else {
+    for (int i = 0; i < kPerThread; ++i)
+      pf[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, tid * 16, kThreads * 16 * i, 2));
+  };
+  auto lds_at = [](int r, int sg) { return r * kRowStride + sg * 16; };
+  // slot of accumulator quad Q among the quads wave w of a group hands over:
+  // Q minus the number of quads below Q that w owns (w owns Q with Q % NWH == w)
+  auto slot = [](int w, int Q) { return Q - (Q + NWH - 1 - w) / NWH; };
+
+  // Scores of a tile go out one iteration later, before the next prefetch is
+  // issued.  Stores and loads share one in-order vector-memory counter: a
+  // store issued after a prefetch would make the wait for that prefetch wait
+  // for the store's completion too.  Slot oq * 4 + e holds the score of row e
+  // of the wave's oq-th own quad (Q = hp + NWH * oq) for this lane.
+  constexpr int kPend = 4 * kQuads / NWH;
+  // with two query blocks per wave the registers are full: the slots live in
+  // this wave's own LDS area (written and read by the wave alone)
+  constexpr bool kPendLds = QW > 1;
+  float pend_r[kPendLds ? 1 : kPend];
+  float* pend_l = iqr + QB * NWH * 2 * 32 + (size_t)wave * kPend * 64;   // [NW][kPend][64]
+  auto set_pend = [&](int k, float v) {
+    if constexpr (kPendLds) pend_l[k * 64 + lane] = v; else pend_r[k] = v;
+  };
+  auto get_pend = [&](int k) -> float {
+    if constexpr (kPendLds) return pend_l[k * 64 + lane]; else return pend_r[k];
+  };
+  // slot (owned quad oq, row e) -> sequence of the score, if the slot holds one
+  auto out_slot = [&](int oq, int e, int& seq) -> bool {
+    const int Q = hp + NWH * oq;                 // this wave's oq-th quad
+    const int r0 = 32 * (grp * QW + (Q >> 2)) + 8 * (Q & 3);
+    if constexpr (TLC == 0) {
+      const int r = r0 + 4 * hf + e;
+      seq = r / t_len;
+      return e % t_len == 0 && r0 < t_tot && r < t_tot;
+    }
+    if (e != 0 || hf != 0) return false;
+    if constexpr (TLC == 1) {
+      seq = r0 / 8;
+      return r0 < t_tot;
+    }
+    const int gq = grp * kQuads + Q, quads = t_len >> 3;
+    seq = gq / quads;
+    return gq % quads == 0 && 8 * gq < t_tot;
+  };
+  auto flush = [&](int tl) {
+    const int64_t col = (int64_t)tl * 32 + cl;
+    const int64_t doc = col / cpd;
+    if ((cl % cpd) != 0 || col >= n_ch || doc >= n_docs) return;
+    // an opaque copy of n_docs keeps the per-slot row offsets from being
+    // hoisted out of the tile loop (they would pin registers for its length)
+    int64_t nd = n_docs;
+    asm volatile("" : "+s"(nd));
 #pragma unroll
-      for (int i = 0; i < kPerThread; ++i) {
-        const int c = tid + kThreads * i;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        pf[i] = col0 + c / kSegs < n_ch ? load16(kbar + (size_t)(col0 + c / kSegs) * kRowElems + (c % kSegs) * 8) : z;
+    for (int oq = 0; oq < kQuads / NWH; ++oq) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        int seq = 0;
+        if (out_slot(oq, e, seq)) out[(size_t)seq * nd + doc] = get_pend(oq * 4 + e);
       }
     }
   };
-  auto swz = [](int r, int sg) { return r * kRowBytes + ((sg ^ (r & 15)) << 4); };
 
   const float inv_h = 1.f / (float)H;
-  int tile = blockIdx.x;
-  if (tile < n_tiles) prefetch(tile);
-  for (; tile < n_tiles; tile += gridDim.x) {
+  // Each workgroup walks a contiguous range of tiles: the 4 scores a tile
+  // writes per sequence are 16 bytes, and the 8 tiles of a 128-byte output
+  // line then share one L2 (an XCD's), which merges them into whole lines.
+  int tile = (int)((int64_t)blockIdx.x * n_tiles / gridDim.x), prev = -1;
+  const int tile_hi = (int)(((int64_t)blockIdx.x + 1) * n_tiles / gridDim.x);
+  if (tile < tile_hi) prefetch(tile);
+  for (; tile < tile_hi; ++tile) {
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
       const int c = tid + kThreads * i;
-      *reinterpret_cast<u32x4*>(ktile + swz(c / kSegs, c % kSegs)) = pf[i];
+      *reinterpret_cast<u32x4*>(ktile + lds_at(c / kSegs, c % kSegs)) = pf[i];
     }
     const bool col_ok = (int64_t)tile * 32 + cl < n_ch;
-    const float ik0 = col_ok ? 1.f / fmaxf(pnorm[0], kEps) : 0.f;
-    const float ik1 = col_ok ? 1.f / fmaxf(pnorm[1], kEps) : 0.f;
+    const float ik0 = 1.f / fmaxf(pnorm[0], kEps), ik1 = 1.f / fmaxf(pnorm[1], kEps);
+    const float ik_ratio = col_ok ? ik0 / ik1 : 0.f;
+    const float ik_last = col_ok ? ik1 : 0.f;
+    if (prev >= 0) flush(prev);
     // the registers are free again: start the next tile before the barrier
-    const int next = tile + gridDim.x;
-    if (next < n_tiles) prefetch(next);
+    const int next = tile + 1;
+    if (next < tile_hi) prefetch(next);
     __syncthreads();
 
-    float sacc[16];
+    f32x16 acc[QW];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+    for (int qw = 0; qw < QW; ++qw) acc[qw] = f32x16{};
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int h = 2 * wave + j;
-      f32x16 acc = {};
+      const int h = 2 * hp + j;
+      // key fragments in groups of KG (fewer live registers with two query blocks)
+      constexpr int KG = QW == 1 ? 4 : 2;
 #pragma unroll
-      for (int k0 = 0; k0 < 8; k0 += 4) {
-        bf16x8 kf[4];
+      for (int k0 = 0; k0 < 8; k0 += KG) {
+        bf16x8 kf[KG];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < KG; ++k) {
           const int kk = k0 + k;
-          kf[k] = *reinterpret_cast<const bf16x8*>(ktile + swz(cl, h * 16 + 8 * (kk >> 2) + 4 * hf + (kk & 3)));
+          kf[k] = *reinterpret_cast<const bf16x8*>(ktile + lds_at(cl, h * 16 + 8 * (kk >> 2) + 4 * hf + (kk & 3)));
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) acc = mfma32(qf[j][k0 + k], kf[k], acc);
+        for (int qw = 0; qw < QW; ++qw) {
+#pragma unroll
+          for (int k = 0; k < KG; ++k) acc[qw] = mfma32(qf[qw][j][k0 + k], kf[k], acc[qw]);
+        }
       }
-      const float ik = j == 0 ? ik0 : ik1;
-      const float* iqh = iqp + (h * 2 + hf) * 16;
+      // x w0/w1 after the first head, x w1 after the second
+      const float ikj = j == 0 ? ik_ratio : ik_last;
 #pragma unroll
-      for (int i = 0; i < 16; i += 4) {
-        const f32x4 iq4 = *reinterpret_cast<const f32x4*>(iqh + i);
+      for (int qw = 0; qw < QW; ++qw) {
+        const float* tab = iqr + (((grp * QW + qw) * NWH + hp) * 2 + hf) * 32 + 16 * j;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sacc[i + e] += acc[i + e] * (iq4[e] * ik);
+        for (int i = 0; i < 16; i += 4) {
+          const f32x4 t4 = *reinterpret_cast<const f32x4*>(tab + i);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[qw][i + e] *= t4[e] * ikj;
+        }
       }
     }
-    // Head sum: every wave owns register quad(s) q = wave (mod NW), i.e. the query
-    // rows 8q + 4hf + 0..3, and adds the other waves' partials of that quad.
-    // slot of quad q among the quads not owned by wave w: q - (number of owned quads below q)
-    auto slot = [](int w, int q) { return q - (q + NW - 1 - w) / NW; };
+    // Head sum: wave hp of a group owns its accumulator quads Q = qw*4 + q with
+    // Q % NWH == hp (query rows 32*qb + 8q + 4hf + 0..3) and adds the other
+    // head pairs' partials of those quads.
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (q % NW != wave)
-        part[(wave * kSlots + slot(wave, q)) * 64 + lane] = f32x4{sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]};
+    for (int Q = 0; Q < kQuads; ++Q)
+      if (Q % NWH != hp)
+        part[(wave * kSlotsAlloc + slot(hp, Q)) * 64 + lane] =
+            f32x4{acc[Q >> 2][4 * (Q & 3)], acc[Q >> 2][4 * (Q & 3) + 1], acc[Q >> 2][4 * (Q & 3) + 2],
+                  acc[Q >> 2][4 * (Q & 3) + 3]};
     __syncthreads();
-    const int64_t col = (int64_t)tile * 32 + cl;
-    const bool writer = (cl % cpd) == 0 && col < n_ch;
-    const int64_t doc = col / cpd;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (q % NW != wave || 8 * q >= t_tot) continue;
-      float v[4] = {sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]};
+    for (int Q = 0; Q < kQuads; ++Q) {
+      const int qb = grp * QW + (Q >> 2), q = Q & 3;
+      const int r0 = 32 * qb + 8 * q;            // first query row of the quad
+      if (Q % NWH != hp || r0 >= t_tot) continue;
+      float v[4] = {acc[Q >> 2][4 * q], acc[Q >> 2][4 * q + 1], acc[Q >> 2][4 * q + 2], acc[Q >> 2][4 * q + 3]};
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        if (w == wave) continue;
-        const f32x4 pv = part[(w * kSlots + slot(w, q)) * 64 + lane];
+      for (int w = 0; w < NWH; ++w) {
+        if (w == hp) continue;
+        const f32x4 pv = part[((grp * NWH + w) * kSlotsAlloc + slot(w, Q)) * 64 + lane];
         v[0] += pv[0];
         v[1] += pv[1];
         v[2] += pv[2];
         v[3] += pv[3];
       }
       // max over each sequence's rows, then over the document's chunks
-      if (t_len <= 4) {
-        for (int e0 = 0; e0 < 4; e0 += t_len) {
-          float m = v[e0];
-          for (int e = 1; e < t_len; ++e) m = fmaxf(m, v[e0 + e]);
-          m = doc_max_dpp(m, cpd) * inv_h;
-          const int r = 8 * q + 4 * hf + e0;
-          if (writer && r < t_tot && doc < n_docs) out[(size_t)(r / t_len) * n_docs + doc] = m;
+      if constexpr (TLC == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (e % t_len != 0) continue;
+          float m = v[e];
+          if (e + 1 < 4 && t_len >= 2) m = fmaxf(m, v[e + 1]);
+          if (e + 3 < 4 && t_len >= 4) m = fmaxf(fmaxf(m, v[e + 2]), v[e + 3]);
+          set_pend((Q / NWH) * 4 + e, doc_max_dpp(m, cpd) * inv_h);
         }
       } else {
         float m = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
         m = fmaxf(m, __shfl_xor(m, 32));
-        if (t_len == 8) {
-          m = doc_max_dpp(m, cpd) * inv_h;
-          if (writer && hf == 0 && doc < n_docs) out[(size_t)q * n_docs + doc] = m;
-        } else {
-          qmax[q * 64 + lane] = m;
-        }
+        if constexpr (TLC == 1)
+          set_pend((Q / NWH) * 4, doc_max_dpp(m, cpd) * inv_h);
+        else
+          qmax[(qb * 4 + q) * 64 + lane] = m;
       }
     }
-    if (t_len >= 16) {
-      // a sequence spans t_len / 8 quads: the owner of its first quad combines them
+    if constexpr (TLC == 2) {
+      // a sequence spans t_len / 8 quads, possibly of several query blocks:
+      // the owner of its first quad combines them
       __syncthreads();
       const int quads = t_len >> 3;
-      for (int q0 = 0; q0 < 4 && 8 * q0 < t_tot; q0 += quads) {
-        if (q0 % NW != wave) continue;
-        float m = qmax[q0 * 64 + lane];
-        for (int qq = q0 + 1; qq < q0 + quads; ++qq) m = fmaxf(m, qmax[qq * 64 + lane]);
-        m = doc_max_dpp(m, cpd) * inv_h;
-        if (writer && hf == 0 && doc < n_docs) out[(size_t)(8 * q0 / t_len) * n_docs + doc] = m;
+#pragma unroll
+      for (int Q = 0; Q < kQuads; ++Q) {
+        const int gq = grp * kQuads + Q;         // quad index over all query blocks
+        if (Q % NWH != hp || gq % quads != 0 || 8 * gq >= t_tot) continue;
+        float m = qmax[gq * 64 + lane];
+        for (int qq = gq + 1; qq < gq + quads; ++qq) m = fmaxf(m, qmax[qq * 64 + lane]);
+        set_pend((Q / NWH) * 4, doc_max_dpp(m, cpd) * inv_h);
       }
     }
+    prev = tile;
   }
+  if (prev >= 0) flush(prev);
 }
 
 // ---------------------------------------------------------------------------
@@ -633,6 +726,7 @@ RoutePath pick(int batch, int q_len, int heads, int dim, int cpd, msa_dtype dt) 
   const bool small_t = q_len <= 32 && (32 % q_len) == 0;
   const bool t32 = q_len % 32 == 0;
   if (t_tot <= 32 && small_t && (heads == 2 || heads == 4 || heads == 8)) return RoutePath::Scan;
+  if (t_tot <= 128 && (small_t || t32) && heads == 8) return RoutePath::Scan;
   if (t_tot <= kStreamMaxRows && (small_t || t32)) return RoutePath::Stream;
   if (t32 && heads <= kMaxHeads) return RoutePath::Tiled;
   if (small_t) return RoutePath::Stream;
@@ -671,25 +765,39 @@ hipError_t launch_route(const void* q_r, const void* kbar_r, const float* knorm,
                                 doc_scores, s);
   if (path == RoutePath::Scan) {
     const int n_tiles = (int)((n_ch + 31) / 32);
-    const int nw = heads / 2;
-    const int slots = nw == 1 ? 1 : 4 - 4 / nw;
-    const size_t smem = (size_t)32 * heads * kDim * 2 + (size_t)nw * slots * 64 * 16 + 4 * 64 * 4 +
-                        (size_t)heads * 32 * 4;
+    const int qb = (t_tot + 31) / 32 == 3 ? 4 : (t_tot + 31) / 32;
     const int n_cu = device_cu_count();
-    const unsigned grid = (unsigned)std::min<int64_t>(n_tiles, (int64_t)n_cu * 2);
-    auto go = [&](auto kern) {
+    auto go = [&](auto kern, int nwh, int qw, int g) {
+      const int nw = nwh * g, quads = 4 * qw;
+      const int slots = std::max(1, quads - quads / nwh);
+      const int blocks = qw * g;
+      const size_t pend = qw > 1 ? (size_t)nw * (4 * quads / nwh) * 64 * 4 : 0;
+      const size_t smem = (size_t)32 * (heads * kDim * 2 + 16) + (size_t)nw * slots * 64 * 16 +
+                          (size_t)blocks * 4 * 64 * 4 + (size_t)blocks * nwh * 2 * 32 * 4 + pend;
       static const hipError_t attr = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, 80 * 1024);
+          reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
       if (attr != hipSuccess) return attr;
-      hipLaunchKernelGGL(kern, dim3(grid), dim3(heads * 32), smem, s, q, k, knorm, t_tot, q_len, n_ch,
+      const int per_cu = (qw == 1 && g == 1) ? 2 : 1;
+      const unsigned grid = (unsigned)std::min<int64_t>(n_tiles, (int64_t)n_cu * per_cu);
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(nw * 64), smem, s, q, k, knorm, t_tot, q_len, n_ch,
                          n_docs, cpd, n_tiles, doc_scores);
       return hipGetLastError();
     };
-    switch (heads) {
-      case 2: return go(route_scan_kernel<2>);
-      case 4: return go(route_scan_kernel<4>);
-      default: return go(route_scan_kernel<8>);
+    const int tlc = q_len <= 4 ? 0 : q_len == 8 ? 1 : 2;
+#define MSA_SCAN(H, QW, G, NWH)                                                  \
+  switch (tlc) {                                                                 \
+    case 0: return go(route_scan_kernel<H, QW, G, 0>, NWH, QW, G);              \
+    case 1: return go(route_scan_kernel<H, QW, G, 1>, NWH, QW, G);              \
+    default: return go(route_scan_kernel<H, QW, G, 2>, NWH, QW, G);             \
+  }
+    if (qb == 1) {
+      if (heads == 2) MSA_SCAN(2, 1, 1, 1)
+      if (heads == 4) MSA_SCAN(4, 1, 1, 2)
+      MSA_SCAN(8, 1, 1, 4)
     }
+    if (qb == 2) MSA_SCAN(8, 1, 2, 4)
+    MSA_SCAN(8, 2, 2, 4)
+#undef MSA_SCAN
   }
   if (path == RoutePath::Stream) {
     const unsigned grid = (unsigned)((n_ch + 31) / 32);

@@ -134,6 +134,16 @@ def _route_case(batch, q_len, heads, dim, n_docs, cpd, dtype, seed, planted=None
     (2, 2, 8, 128, 200, 1, torch.bfloat16),
     (32, 1, 8, 128, 2048, 8, torch.bfloat16),     # decode: 32 sequences x 1 token
     (2, 16, 8, 128, 100, 32, torch.bfloat16),     # 32 chunks per document
+    # HBM scan path with 2 and 4 query blocks of 32 rows (8 heads)
+    (4, 16, 8, 128, 150, 8, torch.bfloat16),      # 64 rows, 16-token sequences
+    (1, 64, 8, 128, 150, 8, torch.bfloat16),      # one sequence over both wave groups
+    (1, 128, 8, 128, 170, 8, torch.bfloat16),     # one sequence over four query blocks
+    (3, 32, 8, 128, 90, 8, torch.bfloat16),       # 96 rows: the fourth block is empty
+    (128, 1, 8, 128, 60, 8, torch.bfloat16),      # 128 single-token sequences
+    (20, 4, 8, 128, 61, 4, torch.bfloat16),       # 80 rows, 4 chunks per document
+    (9, 8, 8, 128, 45, 16, torch.bfloat16),       # 72 rows, 16 chunks per document
+    (5, 16, 8, 128, 33, 32, torch.bfloat16),      # 80 rows, 32 chunks per document
+    (33, 2, 8, 128, 70, 2, torch.bfloat16),       # 66 rows, 2 chunks per document
 ])
 def test_route_parity(batch, q_len, heads, dim, n_docs, cpd, dtype):
     case(f"route B={batch} T={q_len} H={heads} d={dim} N={n_docs} C={cpd} {dtype}")
@@ -148,6 +158,32 @@ def test_route_parity(batch, q_len, heads, dim, n_docs, cpd, dtype):
     assert err.max() <= ROUTE_ATOL
     # the design target is far tighter than the tolerance: products are exact in fp32
     assert err.max() <= 2e-5
+
+
+@pytest.mark.parametrize("batch,q_len", [(1, 1), (4, 32)])
+def test_route_scan_large_bank_sampled(batch, q_len):
+    """The 100M-token shard's bank (195,313 documents x 8 chunks x 8 heads x 128,
+    3.2 GB bf16) in the launch configuration of the scan; the scores of sampled
+    documents against the oracle on those documents' chunks."""
+    case(f"route scan large bank B={batch} T={q_len} (sampled)")
+    n_docs, cpd = 195313, 8
+    g = torch.Generator(device=DEV)
+    g.manual_seed(11 + batch)
+    kbar = torch.empty((n_docs * cpd, 8, 128), device=DEV, dtype=torch.bfloat16)
+    for lo in range(0, n_docs * cpd, 1 << 18):                 # slabs: bounded fp32 temporaries
+        hi = min(n_docs * cpd, lo + (1 << 18))
+        kbar[lo:hi] = torch.randn((hi - lo, 8, 128), generator=g, device=DEV).to(torch.bfloat16)
+    norm = torch.linalg.vector_norm(kbar.float(), dim=-1).contiguous()
+    q_r = torch.randn((batch, q_len, 8, 128), generator=g, device=DEV).to(torch.bfloat16)
+    scores = msa.msa_route_scores(q_r, kbar, norm, cpd)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(batch)
+    docs = np.unique(np.concatenate([[0, 1, n_docs // 2, n_docs - 1], rng.integers(0, n_docs, 60)]))
+    rows = torch.as_tensor((docs[:, None] * cpd + np.arange(cpd)).ravel(), device=DEV)
+    ref = route_scores(to_f64(q_r), to_f64(kbar[rows]), cpd)
+    got = to_f64(scores)[:, docs]
+    assert np.abs(got - ref).max() <= 2e-5
+    del kbar
 
 
 def test_route_zero_rows():
