@@ -17,6 +17,19 @@ Per-kernel durations are measured with HIP events on the stream the kernels
 run on; `roofline` describes the kernel with the largest share of the step.
 `cpu_baseline` times the float64 CPU oracle on a bounded sample of the same
 workload and scales it to the full step.
+
+Profiles (run on the GPU, summaries land in profiles/):
+    rocprofv3 --kernel-trace --stats --output-format csv -d D -o run -- python3 bench.py --steps 5 --no-cpu-baseline
+    python bench.py --summarize-stats D/run_kernel_stats.csv profiles/<name>.md "<title>" "<command>"
+HBM traffic of each stage (`roofline.traffic`): four counter runs into DIR,
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/copy_fetch -o run -- python3 bench.py --copy-probe
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/copy_write -o run -- python3 bench.py --copy-probe
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/<workload>_fetch -o run -- python3 bench.py --workload <workload> --steps 2 --warmup 1 --no-cpu-baseline
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/<workload>_write -o run -- python3 bench.py --workload <workload> --steps 2 --warmup 1 --no-cpu-baseline
+then `python bench.py --summarize-traffic DIR`.  The copy probe moves a known
+1 GiB each way; the ratio of that to what the counters read scales every
+kernel's counters to bytes.  A stage's entry is kept only while its source
+file is unchanged (sha256 recorded beside it).
 """
 
 import argparse
@@ -42,6 +55,13 @@ def parse():
     p.add_argument("--workload", choices=["prefill", "decode"], default="prefill")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    # profiling helpers (see "Profiles" in the module docstring)
+    p.add_argument("--copy-probe", action="store_true",
+                   help="run a plain elementwise 1 GiB read + 1 GiB write five times and exit")
+    p.add_argument("--summarize-stats", nargs=4, metavar=("STATS_CSV", "OUT_MD", "TITLE", "COMMAND"),
+                   help="write a markdown summary of a rocprofv3 --stats kernel_stats.csv and exit")
+    p.add_argument("--summarize-traffic", metavar="DIR",
+                   help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs under DIR into profiles/traffic.json")
     return p.parse_args()
 
 
@@ -108,15 +128,132 @@ def kernel_source_sha(src_file):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(stage, src_file, launches_per_step):
+# stage -> (kernel-name pattern, source file), per workload
+STAGE_KERNELS = {
+    "prefill": {"pool": ("pool_kernel", "pool.hip"), "route": ("route_", "route.hip"),
+                "topk": ("topk", "topk.hip"), "gather": ("gather", "gather.hip"),
+                "attn": ("attn_prefill", "attn_prefill.hip")},
+    "decode": {"route": ("route_", "route.hip"), "topk": ("topk", "topk.hip"),
+               "gather": ("gather", "gather.hip"), "attn": ("attn_decode", "attn_decode.hip")},
+}
+COPY_PROBE_BYTES = 1 << 30
+
+
+def measured_traffic(workload, stage):
+    """HBM bytes per launch of `stage` from profiles/traffic.json, or None when
+    absent or taken on a different version of the stage's source."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        rec = json.load(f).get(stage)
-    if not rec or rec.get("source_sha") != kernel_source_sha(src_file):
+        rec = json.load(f).get(workload, {}).get(stage)
+    if not rec or rec.get("source_sha") != kernel_source_sha(STAGE_KERNELS[workload][stage][1]):
         return None
     return rec["bytes_per_launch"]
+
+
+def _counter_rows(run_dir):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _per_kernel_median(rows):
+    """kernel name -> median of the counter over its dispatches (KiB)."""
+    by = {}
+    for r in rows:
+        by.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sorted(v)[len(v) // 2] for k, v in by.items()}
+
+
+def _short_kernel(name):
+    import re
+    m = re.search(r"msa::\(anonymous namespace\)::([a-z_0-9]+(?:<[^>(]*>)?)", name)
+    return m.group(1) if m else name
+
+
+def summarize_traffic(d):
+    copy = {}
+    for kind in ("fetch", "write"):
+        med = _per_kernel_median(_counter_rows(os.path.join(d, f"copy_{kind}")))
+        probe = [v for k, v in med.items() if "neg" in k]
+        if not probe:
+            raise SystemExit(f"no copy-probe kernel in {d}/copy_{kind}")
+        copy[kind] = probe[0]
+    fetch_factor = COPY_PROBE_BYTES / (copy["fetch"] * 1024)
+    write_factor = COPY_PROBE_BYTES / (copy["write"] * 1024)
+    out = {"calibration": {"copy_probe_bytes_each_way": COPY_PROBE_BYTES, "copy_fetch_kib": copy["fetch"],
+                           "copy_write_kib": copy["write"], "fetch_factor": fetch_factor,
+                           "write_factor": write_factor}}
+    md = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+          "Commands (repository root, one MI355X; DIR = gpurun_out/traffic):", "", "```"]
+    md += ["export TMPDIR=/tmp",
+           "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/copy_fetch -o run -- python3 bench.py --copy-probe",
+           "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/copy_write -o run -- python3 bench.py --copy-probe"]
+    for wl in STAGE_KERNELS:
+        md += [f"rocprofv3 --pmc {c} --output-format csv -d DIR/{wl}_{c.split('_')[0].lower()} -o run -- "
+               f"python3 bench.py --workload {wl} --steps 2 --warmup 1 --no-cpu-baseline"
+               for c in ("FETCH_SIZE", "WRITE_SIZE")]
+    md += ["python bench.py --summarize-traffic DIR", "```", "",
+           f"Calibration: a 1 GiB elementwise read+write reads {copy['fetch']:.0f} KiB (FETCH_SIZE) and writes "
+           f"{copy['write']:.0f} KiB (WRITE_SIZE); factors {fetch_factor:.4f} and {write_factor:.4f} turn "
+           "counter KiB into bytes.", "",
+           "| workload | stage | kernels | read MB | written MB | total MB per launch |", "|---|---|---|---|---|---|"]
+    for wl, stages in STAGE_KERNELS.items():
+        fm = _per_kernel_median(_counter_rows(os.path.join(d, f"{wl}_fetch")))
+        wm = _per_kernel_median(_counter_rows(os.path.join(d, f"{wl}_write")))
+        if not fm or not wm:
+            continue
+        out[wl] = {}
+        for stage, (pat, src) in stages.items():
+            names = sorted(k for k in fm if pat in k and "msa::" in k)
+            if not names:
+                continue
+            rd = sum(fm[k] for k in names) * 1024 * fetch_factor
+            wr = sum(wm.get(k, 0.0) for k in names) * 1024 * write_factor
+            out[wl][stage] = {"source_sha": kernel_source_sha(src), "read_bytes": rd, "write_bytes": wr,
+                              "bytes_per_launch": rd + wr, "kernels": names}
+            short = ", ".join(sorted({_short_kernel(n) for n in names}))
+            md.append(f"| {wl} | {stage} | `{short}` | {rd / 1e6:.1f} | {wr / 1e6:.1f} | {(rd + wr) / 1e6:.1f} |")
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    with open(os.path.join(ROOT, "profiles", "hbm-traffic_prefill-and-decode-steps.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    print(json.dumps(out, indent=1))
+
+
+def summarize_stats(csv_path, out_md, title, command):
+    import csv
+    with open(csv_path) as fh:
+        rows = list(csv.DictReader(fh))
+    ours, other_ns = [], 0
+    for r in rows:
+        if "msa::" not in r["Name"]:
+            other_ns += int(r["TotalDurationNs"])
+            continue
+        ours.append((_short_kernel(r["Name"]), int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]),
+                     float(r["MaxNs"]), int(r["TotalDurationNs"])))
+    with open(out_md, "w") as f:
+        f.write(f"# {title}\n\nCommand (repository root, one MI355X):\n\n```\n{command}\n```\n\n")
+        f.write("| kernel | calls | avg us | min us | max us | total us |\n|---|---|---|---|---|---|\n")
+        for name, c, a, mn, mx, t in sorted(ours, key=lambda x: -x[5]):
+            f.write(f"| `{name}` | {c} | {a / 1e3:.1f} | {mn / 1e3:.1f} | {mx / 1e3:.1f} | {t / 1e3:.1f} |\n")
+        f.write(f"\nOther kernels (torch input synthesis, copies): {other_ns / 1e3:.1f} us total.\n")
+
+
+def copy_probe():
+    import torch
+    n = COPY_PROBE_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print("copy probe done", float(dst[0]))
 
 
 # ---------------------------------------------------------------------------
@@ -125,9 +262,6 @@ def measured_traffic(stage, src_file, launches_per_step):
 
 class Step:
     """Preallocated buffers and the sequence of ABI calls of one step."""
-
-    STAGE_SRC = {"pool": "pool.hip", "route": "route.hip", "topk": "topk.hip", "gather": "gather.hip",
-                 "attn": "attn_prefill.hip"}
 
     def __init__(self, cfg, workload, seed, dev):
         import torch
@@ -271,9 +405,19 @@ def cpu_baseline(step, cfg, workload):
 
 def main():
     args = parse()
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic)
+        return
+    if args.copy_probe:
+        copy_probe()
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path; see DESIGN.md for how it would shard)", file=sys.stderr)
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported. The path would "
+              "shard documents across GPUs (each routes its shard, one all-gather of k candidates per "
+              "sequence, a final top-k), but only the single-GPU share is built and timed.", file=sys.stderr)
         sys.exit(2)
     import torch
     import msa_inputs as mi
@@ -317,7 +461,7 @@ def main():
     roof = {k: stages[dom][k] for k in ("bound", "achieved", "peak", "unit", "frac")}
     roof["kernel"] = dom
     roof["avg_launch_ms"] = stages[dom]["avg_launch_ms"]
-    roof["traffic"] = measured_traffic(dom, Step.STAGE_SRC[dom], stages[dom]["launches_per_step"])
+    roof["traffic"] = measured_traffic(args.workload, dom)
 
     tokens = cfg.batch * cfg.q_len
     online_ms = sum(stages[s]["ms_per_step"] for s in stages if s != "pool")
