@@ -6,18 +6,28 @@
 //
 // HBM-bound: every key and value row is read once.  The query columns are
 // the (token, head) pairs of one KV group (T * group <= 32), so each K/V row
-// is read once for all query heads that share it.  The keys of a sequence
-// are cut into splits of 128; a workgroup (4 waves) owns one split and each
-// wave 32 keys of it:
-//   * K rows go straight from HBM into MFMA operands (16-byte loads, one
-//     64-byte run per lane per half head),
-//   * V rows are staged in the wave's own LDS region as interleaved key pairs
-//     (see attn_prefill.hip) to form the V^T operand,
+// is read once for all query heads that share it.  Keys are cut into splits
+// of 128, and wave w of a workgroup takes keys 32w .. 32w+31 of each split:
+//   * K and V rows are read whole (16 lanes x 16 bytes per 256-byte row, so a
+//     wave instruction covers 4 rows): reading a K row as MFMA operand pieces
+//     straight from HBM (32 rows x 32 bytes per instruction) costs ~30% of
+//     the bandwidth,
+//   * K rows go through the wave's own LDS region (row pitch padded to 272
+//     bytes for conflict-free operand reads) into the K operand; V rows are
+//     staged there as interleaved key pairs to form the V^T operand,
 //   * S^T = K . Q^T and O^T = V^T . P^T run on bf16 MFMA in the same
 //     lane-owns-a-query orientation as the prefill kernel.
-// The four waves' (max, sum, O) partials merge through LDS, the workgroup
-// writes one float32 partial per split, and attn_decode_combine merges the
-// splits (the standard log-sum-exp merge) into bf16 output and the LSE.
+// A workgroup owns one (sequence, KV head) and a contiguous run of splits.
+// Each wave keeps an online softmax over its slices of those splits and has
+// two register sets of K/V rows: the loads of the next split are in flight
+// while the current one is computed, so HBM sees a steady stream instead of
+// a burst per short workgroup.  The four waves merge through LDS at the end.
+// With at least one (sequence, KV head) per CU a workgroup takes all splits
+// and writes the bf16 output directly; with fewer, each pair is cut into P
+// runs that write float32 partials and attn_decode_combine merges them (the
+// log-sum-exp merge).
+#include <algorithm>
+
 #include "internal.h"
 
 namespace msa {
@@ -28,6 +38,8 @@ constexpr int kWaves = 4;
 constexpr int kSplitKeys = kWaves * 32;
 constexpr int kVStride = 144;  // words per key-pair row (128 + pad)
 constexpr int kVRegionWords = 16 * kVStride;
+constexpr int kKPitch = 272;   // bytes per K row in LDS (256 + pad)
+constexpr int kKRegionBytes = 32 * kKPitch;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -53,53 +65,63 @@ struct Rows {
   }
 };
 
-__global__ __launch_bounds__(kWaves * 64) void attn_decode_kernel(
+struct KVRegs {
+  u32x4 kw[8];         // K rows of the wave's 32 keys, 16 bytes at a time
+  u32x4 va[4], vb[4];  // V rows of its 16 key pairs, 16 bytes at a time
+};
+// K piece st of a lane: row 8*(st & 3) + 2*(lane >> 4) + (st >> 2) of the wave's
+// 32 keys, 16-byte segment lane & 15.
+__device__ __forceinline__ int krow_of(int st, int lane) { return 8 * (st & 3) + 2 * (lane >> 4) + (st >> 2); }
+
+__global__ __launch_bounds__(kWaves * 64, 1) void attn_decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_sel,
     const uint16_t* __restrict__ v_sel, int mem_len, const uint16_t* __restrict__ k_loc,
     const uint16_t* __restrict__ v_loc, int loc_len, int batch, int q_len, int heads_q, int heads_kv,
-    float scale_log2, int n_split, float* __restrict__ part_o, float* __restrict__ part_ml) {
+    float scale_log2, int n_split, int n_part, int per_part, float* __restrict__ part_o,
+    float* __restrict__ part_ml, uint16_t* __restrict__ out, float* __restrict__ lse) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   uint32_t* vsm = reinterpret_cast<uint32_t*>(smem_raw);     // [wave][16 pairs][kVStride]
   float* cb = reinterpret_cast<float*>(smem_raw);            // reused: [wave][nq][kD]
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int cl = lane & 31, hf = lane >> 5;
   const int group = heads_q / heads_kv;
   const int nq = q_len * group;
 
   int bid = blockIdx.x;
-  const int split = bid % n_split;
-  bid /= n_split;
+  const int part = bid % n_part;
+  bid /= n_part;
   const int g = bid % heads_kv;
   const int b = bid / heads_kv;
+  const int s_lo = part * per_part;
+  const int s_hi = min(n_split, s_lo + per_part);
 
   const int kend = mem_len + loc_len;
   const int causal0 = kend - q_len;  // token tt sees kappa < causal0 + tt + 1
-  const int k0 = split * kSplitKeys + wave * 32;
   const Rows kr{k_sel, k_loc, mem_len, loc_len, heads_kv, b, g};
   const Rows vr{v_sel, v_loc, mem_len, loc_len, heads_kv, b, g};
   const u32x4 z = {0u, 0u, 0u, 0u};
 
-  // issue all global loads first: V pairs (staging), K operand, Q^T operand
-  u32x4 va[4], vb[4];
+  // Loads are unconditional (a branch per load would leave the compiler unable
+  // to count them and make it wait for all of them): keys past the end read
+  // the last key's row, whose scores are masked to -inf, so its V rows get
+  // weight 0.
+  auto load = [&](KVRegs& r, int sp) {
+    const int k0 = sp * kSplitKeys + wave * 32;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int task = lane + 64 * i;
-    const int p = task >> 4, seg = task & 15;
-    const int ka = k0 + 2 * p;
-    va[i] = ka < kend ? load16(vr.row(ka) + seg * 8) : z;
-    vb[i] = ka + 1 < kend ? load16(vr.row(ka + 1) + seg * 8) : z;
-  }
-  bf16x8 kf[8];
-  {
-    const int key = k0 + cl;
-    const bool ok = key < kend;
-    const uint16_t* src = ok ? kr.row(key) : k_loc;
+    for (int i = 0; i < 4; ++i) {
+      const int task = lane + 64 * i;
+      const int pr = task >> 4, seg = task & 15;
+      const int ka = min(k0 + 2 * pr, kend - 1), kb = min(k0 + 2 * pr + 1, kend - 1);
+      r.va[i] = load16_stream(vr.row(ka) + seg * 8);
+      r.vb[i] = load16_stream(vr.row(kb) + seg * 8);
+    }
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      kf[s] = as_bf16x8(ok ? load16(src + 64 * (s >> 2) + 32 * hf + 8 * (s & 3)) : z);
-  }
+    for (int st = 0; st < 8; ++st)
+      r.kw[st] = load16_stream(kr.row(min(k0 + krow_of(st, lane), kend - 1)) + (lane & 15) * 8);
+  };
+
   const bool col_ok = cl < nq;
   const int tt = col_ok ? cl / group : 0;
   const int h = g * group + (col_ok ? cl % group : 0);
@@ -107,81 +129,123 @@ __global__ __launch_bounds__(kWaves * 64) void attn_decode_kernel(
   {
     const uint16_t* src = q + (((size_t)b * q_len + tt) * heads_q + h) * kD;
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      qf[s] = as_bf16x8(col_ok ? load16(src + 64 * (s >> 2) + 32 * hf + 8 * (s & 3)) : z);
+    for (int st = 0; st < 8; ++st)
+      qf[st] = as_bf16x8(col_ok ? load16(src + 64 * (st >> 2) + 32 * hf + 8 * (st & 3)) : z);
   }
-
-  // S^T = K . Q^T  (32 keys x 32 query columns)
-  f32x16 s = {};
-#pragma unroll
-  for (int st = 0; st < 8; ++st) s = mfma32(kf[st], qf[st], s);
-
-  // stage V as key pairs in this wave's LDS region
-  uint32_t* vreg = vsm + wave * kVRegionWords;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int task = lane + 64 * i;
-    const int p = task >> 4, seg = task & 15;
-    u32x4 w0, w1;
-    w0[0] = pair_lo(va[i][0], vb[i][0]);
-    w0[1] = pair_hi(va[i][0], vb[i][0]);
-    w0[2] = pair_lo(va[i][1], vb[i][1]);
-    w0[3] = pair_hi(va[i][1], vb[i][1]);
-    w1[0] = pair_lo(va[i][2], vb[i][2]);
-    w1[1] = pair_hi(va[i][2], vb[i][2]);
-    w1[2] = pair_lo(va[i][3], vb[i][3]);
-    w1[3] = pair_hi(va[i][3], vb[i][3]);
-    *reinterpret_cast<u32x4*>(&vreg[p * kVStride + seg * 8]) = w0;
-    *reinterpret_cast<u32x4*>(&vreg[p * kVStride + seg * 8 + 4]) = w1;
-  }
-
-  // mask, max, probabilities
   const int lim = min(kend, causal0 + tt + 1);
-  float m = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float v = s[i] * scale_log2;
-    if (k0 + acc_row(i, hf) >= lim) v = -INFINITY;
-    s[i] = v;
-    m = fmaxf(m, v);
-  }
-  m = fmaxf(m, __shfl_xor(m, 32));
-  const float mref = m == -INFINITY ? 0.f : m;
-  float lsum = 0.f;
-  bf16x8 pf[2];
-#pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2) {
-    u32x4 w;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float p0 = fast_exp2(s[8 * s2 + 2 * e] - mref);
-      const float p1 = fast_exp2(s[8 * s2 + 2 * e + 1] - mref);
-      lsum += p0 + p1;
-      w[e] = pack_bf16x2(p0, p1);
-    }
-    pf[s2] = as_bf16x8(w);
-  }
-  const float l = lsum + __shfl_xor(lsum, 32);
-  __syncthreads();
 
-  // O^T = V^T . P^T  (128 d x 32 query columns)
+  uint32_t* vreg = vsm + wave * kVRegionWords;
+  uint8_t* kreg = smem_raw + (size_t)kWaves * kVRegionWords * 4 + (size_t)wave * kKRegionBytes;
   f32x16 o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+  float m = -INFINITY;   // running max of the scaled scores (log2 units)
+  float lh = 0.f;        // this lane half's running sum
+
+  auto process = [&](const KVRegs& r, int sp) {
+    const int k0 = sp * kSplitKeys + wave * 32;
+    // K rows into this wave's LDS region, then the K operand: lane (key cl,
+    // half hf) takes d-slots 64*(st/4) + 32*hf + 8*(st%4) .. +8 (the order of Q^T)
 #pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2) {
-    const uint32_t* vrow = &vreg[(8 * s2 + 2 * hf) * kVStride];
+    for (int st = 0; st < 8; ++st)
+      *reinterpret_cast<u32x4*>(kreg + krow_of(st, lane) * kKPitch + (lane & 15) * 16) = r.kw[st];
+    bf16x8 kf[8];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int d = db * 32 + cl;
-      u32x4 w;
-      w[0] = vrow[d];
-      w[1] = vrow[kVStride + d];
-      w[2] = vrow[4 * kVStride + d];
-      w[3] = vrow[5 * kVStride + d];
-      o[db] = mfma32(as_bf16x8(w), pf[s2], o[db]);
+    for (int st = 0; st < 8; ++st)
+      kf[st] = *reinterpret_cast<const bf16x8*>(kreg + cl * kKPitch + (8 * (st >> 2) + 4 * hf + (st & 3)) * 16);
+    // S^T = K . Q^T  (32 keys x 32 query columns)
+    f32x16 s = {};
+#pragma unroll
+    for (int st = 0; st < 8; ++st) s = mfma32(kf[st], qf[st], s);
+    // V key pairs into this wave's LDS region (read back by the same wave only)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int task = lane + 64 * i;
+      const int pr = task >> 4, seg = task & 15;
+      u32x4 w0, w1;
+      w0[0] = pair_lo(r.va[i][0], r.vb[i][0]);
+      w0[1] = pair_hi(r.va[i][0], r.vb[i][0]);
+      w0[2] = pair_lo(r.va[i][1], r.vb[i][1]);
+      w0[3] = pair_hi(r.va[i][1], r.vb[i][1]);
+      w1[0] = pair_lo(r.va[i][2], r.vb[i][2]);
+      w1[1] = pair_hi(r.va[i][2], r.vb[i][2]);
+      w1[2] = pair_lo(r.va[i][3], r.vb[i][3]);
+      w1[3] = pair_hi(r.va[i][3], r.vb[i][3]);
+      *reinterpret_cast<u32x4*>(&vreg[pr * kVStride + seg * 8]) = w0;
+      *reinterpret_cast<u32x4*>(&vreg[pr * kVStride + seg * 8 + 4]) = w1;
     }
+    // mask, online max, probabilities
+    float mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float v = s[i] * scale_log2;
+      if (k0 + acc_row(i, hf) >= lim) v = -INFINITY;
+      s[i] = v;
+      mt = fmaxf(mt, v);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m, mt);
+    const float mref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m - mref);   // 0 while nothing was visible
+    m = m_new;
+    float lsum = 0.f;
+    bf16x8 pf[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = fast_exp2(s[8 * s2 + 2 * e] - mref);
+        const float p1 = fast_exp2(s[8 * s2 + 2 * e + 1] - mref);
+        lsum += p0 + p1;
+        w[e] = pack_bf16x2(p0, p1);
+      }
+      pf[s2] = as_bf16x8(w);
+    }
+    lh = lh * alpha + lsum;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    }
+    // O^T += V^T . P^T  (128 d x 32 query columns)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const uint32_t* vrow = &vreg[(8 * s2 + 2 * hf) * kVStride];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int d = db * 32 + cl;
+        u32x4 w;
+        w[0] = vrow[d];
+        w[1] = vrow[kVStride + d];
+        w[2] = vrow[4 * kVStride + d];
+        w[3] = vrow[5 * kVStride + d];
+        o[db] = mfma32(as_bf16x8(w), pf[s2], o[db]);
+      }
+    }
+  };
+
+  // Two register sets: the next split's rows load while the current is
+  // computed.  The steady-state body loads unconditionally, so the compiler
+  // can wait for exactly the older set; the last one or two splits are peeled.
+  KVRegs ra, rb;
+  int sp = s_lo;
+  if (sp < s_hi) load(ra, sp);
+  for (; sp + 2 < s_hi; sp += 2) {
+    load(rb, sp + 1);
+    process(ra, sp);
+    load(ra, sp + 2);
+    process(rb, sp + 1);
   }
+  if (sp + 1 < s_hi) {
+    load(rb, sp + 1);
+    process(ra, sp);
+    process(rb, sp + 1);
+  } else if (sp < s_hi) {
+    process(ra, sp);
+  }
+  const float l = lh + __shfl_xor(lh, 32);
   __syncthreads();  // every wave is done with its V region before it is reused
 
   // merge the four waves: cb[wave][n][d], then (m, l) after it
@@ -198,7 +262,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_decode_kernel(
     }
   }
   __syncthreads();
-  const size_t pbase = (((size_t)b * heads_kv + g) * n_split + split) * nq;
+  const size_t pbase = (((size_t)b * heads_kv + g) * n_part + part) * nq;
   for (int idx = tid; idx < nq * kD; idx += kWaves * 64) {
     const int n = idx / kD, d = idx - n * kD;
     float mw[kWaves];
@@ -217,18 +281,28 @@ __global__ __launch_bounds__(kWaves * 64) void attn_decode_kernel(
         lt += mls[(w * nq + n) * 2 + 1] * f;
       }
     }
-    part_o[(pbase + n) * kD + d] = acc;
-    if (d == 0) {
-      part_ml[(pbase + n) * 2] = mx;
-      part_ml[(pbase + n) * 2 + 1] = lt;
+    if (n_part == 1) {
+      // every key of the pair was seen here: normalise and write the output
+      const int tq = n / group, hq = g * group + n % group;
+      out[(((size_t)b * q_len + tq) * heads_q + hq) * kD + d] = f32_to_bf16(acc / lt);
+      if (d == 0 && lse != nullptr)
+        lse[((size_t)b * heads_q + hq) * q_len + tq] = (mx + __log2f(lt)) * kLn2;
+    } else {
+      part_o[(pbase + n) * kD + d] = acc;
+      if (d == 0) {
+        part_ml[(pbase + n) * 2] = mx;
+        part_ml[(pbase + n) * 2 + 1] = lt;
+      }
     }
   }
 }
 
-// Merge the splits of one (sequence, token, query head): one wave, 2 d per lane.
+// Merge the P partials of one (sequence, token, query head): one wave; lanes
+// read the partials' (max, sum) in parallel, then each lane sums 2 d over the
+// partials with the weights broadcast from the lane that read them.
 __global__ __launch_bounds__(256) void attn_decode_combine(
     const float* __restrict__ part_o, const float* __restrict__ part_ml, int batch, int q_len,
-    int heads_q, int heads_kv, int n_split, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    int heads_q, int heads_kv, int n_part, uint16_t* __restrict__ out, float* __restrict__ lse) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t n_rows = (int64_t)batch * q_len * heads_q;
@@ -240,19 +314,31 @@ __global__ __launch_bounds__(256) void attn_decode_combine(
   const int g = h / group;
   const int nq = q_len * group;
   const int n = t * group + (h - g * group);
-  const size_t base = ((size_t)b * heads_kv + g) * n_split;
-  float mx = -INFINITY;
-  for (int sp = 0; sp < n_split; ++sp) mx = fmaxf(mx, part_ml[((base + sp) * nq + n) * 2]);
-  float o0 = 0.f, o1 = 0.f, lt = 0.f;
-  for (int sp = 0; sp < n_split; ++sp) {
-    const size_t pi = (base + sp) * nq + n;
-    const float ms = part_ml[pi * 2];
-    if (ms == -INFINITY) continue;
-    const float f = fast_exp2(ms - mx);
-    lt += part_ml[pi * 2 + 1] * f;
-    const float2 v = *reinterpret_cast<const float2*>(&part_o[pi * kD + 2 * lane]);
-    o0 += v.x * f;
-    o1 += v.y * f;
+  const size_t base = ((size_t)b * heads_kv + g) * n_part;
+  // n_part <= 64: lane p holds partial p
+  const bool has = lane < n_part;
+  const float mp = has ? part_ml[((base + lane) * nq + n) * 2] : -INFINITY;
+  const float lp = has ? part_ml[((base + lane) * nq + n) * 2 + 1] : 0.f;
+  float mx = mp;
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  const float f = (mp == -INFINITY) ? 0.f : fast_exp2(mp - mx);
+  float lt = lp * f;
+  for (int off = 32; off > 0; off >>= 1) lt += __shfl_xor(lt, off);
+  float o0 = 0.f, o1 = 0.f;
+  for (int p0 = 0; p0 < n_part; p0 += 4) {
+    float2 v[4];
+    float w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int pp = min(p0 + j, n_part - 1);
+      w[j] = p0 + j < n_part ? __shfl(f, pp) : 0.f;
+      v[j] = *reinterpret_cast<const float2*>(&part_o[((base + pp) * nq + n) * kD + 2 * lane]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o0 += v[j].x * w[j];
+      o1 += v[j].y * w[j];
+    }
   }
   const float inv = 1.f / lt;
   uint16_t* orow = out + (((size_t)b * q_len + t) * heads_q + h) * kD;
@@ -266,14 +352,30 @@ bool attn_decode_supported(int q_len, int heads_q, int heads_kv, int dim, msa_dt
   return dt == MSA_BF16 && dim == kD && q_len * (heads_q / heads_kv) <= 32;
 }
 
-static int decode_splits(int mem_len, int loc_len) {
+namespace {
+constexpr int kMaxParts = 64;
+
+int decode_splits(int mem_len, int loc_len) {
   return (mem_len + loc_len + kSplitKeys - 1) / kSplitKeys;
 }
 
+// Runs per (sequence, KV head): enough workgroups for one per CU, never more
+// runs than splits, at most kMaxParts.
+int decode_parts(int batch, int heads_kv, int n_split) {
+  const int pairs = batch * heads_kv;
+  int p = device_cu_count() / (pairs > 0 ? pairs : 1);
+  p = std::max(1, std::min({p, n_split, kMaxParts}));
+  return p;
+}
+}  // namespace
+
 size_t attn_decode_workspace(int batch, int q_len, int heads_q, int heads_kv, int mem_len,
                              int loc_len) {
+  const int n_split = decode_splits(mem_len, loc_len);
+  const int n_part = decode_parts(batch, heads_kv, n_split);
+  if (n_part == 1) return 0;
   const size_t nq = (size_t)q_len * (heads_q / heads_kv);
-  const size_t parts = (size_t)batch * heads_kv * decode_splits(mem_len, loc_len) * nq;
+  const size_t parts = (size_t)batch * heads_kv * n_part * nq;
   return parts * (kD + 2) * sizeof(float) + 256;
 }
 
@@ -282,26 +384,33 @@ hipError_t launch_attn_decode(const void* q, const void* k_sel, const void* v_se
                               int q_len, int heads_q, int heads_kv, float scale, void* out,
                               float* lse, void* ws, hipStream_t s) {
   const int n_split = decode_splits(mem_len, loc_len);
+  int n_part = decode_parts(batch, heads_kv, n_split);
+  const int per_part = (n_split + n_part - 1) / n_part;
+  n_part = (n_split + per_part - 1) / per_part;   // no empty runs
   const int nq = q_len * (heads_q / heads_kv);
-  const size_t parts = (size_t)batch * heads_kv * n_split * nq;
+  const size_t parts = (size_t)batch * heads_kv * n_part * nq;
+  if (n_part > 1 && ws == nullptr) return hipErrorInvalidValue;
   float* part_o = static_cast<float*>(ws);
-  float* part_ml = part_o + parts * kD;
-  const size_t smem_v = (size_t)kWaves * kVRegionWords * 4;
+  float* part_ml = n_part > 1 ? part_o + parts * kD : nullptr;
+  const size_t smem_v = (size_t)kWaves * (kVRegionWords * 4 + kKRegionBytes);
   const size_t smem_c = ((size_t)kWaves * nq * kD + (size_t)kWaves * nq * 2) * 4;
   const size_t smem = smem_v > smem_c ? smem_v : smem_c;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(attn_decode_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
       (int)(kWaves * (32 * kD + 64) * 4 > (int)smem_v ? kWaves * (32 * kD + 64) * 4 : (int)smem_v));
   if (attr != hipSuccess) return attr;
-  const unsigned grid = (unsigned)((size_t)batch * heads_kv * n_split);
+  const unsigned grid = (unsigned)((size_t)batch * heads_kv * n_part);
   hipLaunchKernelGGL(attn_decode_kernel, dim3(grid), dim3(kWaves * 64), smem, s,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_sel),
                      static_cast<const uint16_t*>(v_sel), mem_len, static_cast<const uint16_t*>(k_loc),
                      static_cast<const uint16_t*>(v_loc), loc_len, batch, q_len, heads_q, heads_kv,
-                     scale * kLog2e, n_split, part_o, part_ml);
-  const int64_t rows = (int64_t)batch * q_len * heads_q;
-  hipLaunchKernelGGL(attn_decode_combine, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, part_o,
-                     part_ml, batch, q_len, heads_q, heads_kv, n_split, static_cast<uint16_t*>(out), lse);
+                     scale * kLog2e, n_split, n_part, per_part, part_o, part_ml,
+                     static_cast<uint16_t*>(out), lse);
+  if (n_part > 1) {
+    const int64_t rows = (int64_t)batch * q_len * heads_q;
+    hipLaunchKernelGGL(attn_decode_combine, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, part_o,
+                       part_ml, batch, q_len, heads_q, heads_kv, n_part, static_cast<uint16_t*>(out), lse);
+  }
   return hipGetLastError();
 }
 
