@@ -22,8 +22,8 @@
 // conflicts.  Each MFMA group's operand reads are issued before the group
 // (one LDS latency per group, not per MFMA).  K and V rows are fetched with
 // buffer loads: a per-lane byte offset fixed for the whole kernel plus a
-// per-tile scalar offset, so no address arithmetic runs per load except on
-// the last tile and on a tile that straddles the memory/local boundary.  The
+// per-tile scalar offset and a scalar choice of the memory or local rows'
+// resource, so the loads carry no address arithmetic and no branches.  The
 // softmax scale is folded into one FMA before exp2, and probabilities are
 // packed to bf16 by the hardware converter.
 //
@@ -34,9 +34,10 @@
 // LDS tiles, and the two partial softmax states merge through LDS at the end.
 // Splitting the keys inside the workgroup halves the longest workgroup's
 // critical path, which bounds a causal prefill whose longest block needs
-// every key.  Keys are a virtual sequence [memory rows ; local rows]; tiles
-// fully below every query's causal limit skip the mask, tiles beyond the
-// last query's limit are never loaded.  Workgroups are issued longest-first.
+// every key.  Key tiles cover the memory rows, then the local rows (a tile
+// never mixes the two); tiles fully below every query's causal limit skip
+// the mask, tiles beyond the last query's limit are never loaded.
+// Workgroups are issued longest-first.
 #include "internal.h"
 
 namespace msa {
@@ -76,23 +77,16 @@ __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
-// Rows of the virtual key sequence [memory rows ; local rows] of one (sequence, KV head).
+// Memory rows and local rows of one (sequence, KV head), each behind a buffer
+// resource based at the sequence's first row and sized to its rows: a row
+// past the end reads as zeros.
 struct KVRows {
-  __amdgpu_buffer_rsrc_t sel, loc;   // based at the sequence's first row, sized to its rows
-  int mem_len;
+  __amdgpu_buffer_rsrc_t sel, loc;
   uint32_t rs;                       // row stride in bytes (heads_kv * 256)
-  // 16 bytes at byte `in_row` of key row kappa0 + r.  Fast path: the whole tile lies
-  // inside memory or inside local rows and below `kend`, and `voff` = r*rs + in_row.
-  __device__ __forceinline__ u32x4 fast(int kappa0, uint32_t voff) const {
-    if (kappa0 >= mem_len) return bload(loc, voff, (uint32_t)(kappa0 - mem_len) * rs);
-    return bload(sel, voff, (uint32_t)kappa0 * rs);
-  }
-  // Any tile: clamp past `kend`, choose memory or local per row.
-  __device__ __forceinline__ u32x4 slow(int kappa0, int r, uint32_t in_row, int kend) const {
-    const int kappa = min(kappa0 + r, kend - 1);
-    const u32x4 a = bload(sel, (uint32_t)min(kappa, max(mem_len - 1, 0)) * rs + in_row, 0);
-    const u32x4 b = bload(loc, (uint32_t)max(kappa - mem_len, 0) * rs + in_row, 0);
-    return kappa < mem_len ? a : b;
+  // 16 bytes at byte voff of row `row0` of the memory (mem) or local rows; the
+  // choice is uniform, so it is a scalar select and the load has no branch.
+  __device__ __forceinline__ u32x4 load(bool mem, int row0, uint32_t voff) const {
+    return bload(mem ? sel : loc, voff, (uint32_t)row0 * rs);
   }
 };
 
@@ -137,15 +131,22 @@ __global__ __launch_bounds__(NW * 64 * SPLIT, SPLIT == 1 && NW == 4 ? 2 : 1) voi
   const uint32_t loc_bytes = (uint32_t)((size_t)loc_len * rs);
   const KVRows kr{__builtin_amdgcn_make_buffer_rsrc((void*)(k_sel + (mem_len ? sel_rows : 0)), (short)0, sel_bytes, kRsrcWord3),
                   __builtin_amdgcn_make_buffer_rsrc((void*)(k_loc + loc_rows), (short)0, loc_bytes, kRsrcWord3),
-                  mem_len, rs};
+                  rs};
   const KVRows vr{__builtin_amdgcn_make_buffer_rsrc((void*)(v_sel + (mem_len ? sel_rows : 0)), (short)0, sel_bytes, kRsrcWord3),
                   __builtin_amdgcn_make_buffer_rsrc((void*)(v_loc + loc_rows), (short)0, loc_bytes, kRsrcWord3),
-                  mem_len, rs};
+                  rs};
 
-  const int causal0 = mem_len + loc_len - q_len;          // token t sees kappa < causal0 + t + 1
-  const int kend = causal0 + min(t0 + 32, q_len);          // keys needed by the block
-  const int n_tiles = (kend + kKT - 1) / kKT;
-  const int full_below = causal0 + t0 + 1;                 // keys < this are visible to all
+  // Key tiles: first the memory rows (always visible), then the local rows
+  // the block needs; each tile reads rows of one kind only.  Key index kappa
+  // counts [memory rows ; local rows]; token t sees local kappa < causal0 + t + 1.
+  const int causal0 = mem_len + loc_len - q_len;
+  const int n_mt = (mem_len + kKT - 1) / kKT;
+  const int loc_need = loc_len - q_len + min(t0 + 32, q_len);
+  const int n_tiles = n_mt + (loc_need + kKT - 1) / kKT;
+  const int full_below = causal0 + t0 + 1;                 // local keys < this are visible to all
+  auto tile_mem = [&](int tile) { return tile < n_mt; };
+  auto tile_row0 = [&](int tile) { return tile < n_mt ? tile * kKT : (tile - n_mt) * kKT; };
+  auto tile_kappa0 = [&](int tile) { return tile < n_mt ? tile * kKT : mem_len + (tile - n_mt) * kKT; };
 
   // Q^T operand: lane (query cl, half hf), d-slots 64*(s/4) + 32*hf + 8*(s%4) .. +8
   bf16x8 qf[8];
@@ -177,25 +178,19 @@ __global__ __launch_bounds__(NW * 64 * SPLIT, SPLIT == 1 && NW == 4 ? 2 : 1) voi
   };
   const uint32_t v_in_row = goff + (tid & 15) * 16;   // d-block = c % 16 = tid % 16
   u32x4 pk[kKChunks], pv[kVTasks][4];
+  // Branch-free: rows past the block's needs are loaded too (they exist or
+  // read as zeros) and masked; a load per branch would leave the compiler
+  // unable to count the loads in flight and make it wait for all of them.
   auto gload = [&](int tile) {
-    const int kappa0 = tile * kKT;
-    const bool fast = kappa0 + kKT <= kend && (kappa0 >= mem_len || kappa0 + kKT <= mem_len);
-    if (fast) {
+    const bool mem = tile_mem(tile);
+    const int row0 = tile_row0(tile);
 #pragma unroll
-      for (int i = 0; i < kKChunks; ++i) pk[i] = kr.fast(kappa0 + kKRowStep * i, kvoff);
+    for (int i = 0; i < kKChunks; ++i) pk[i] = kr.load(mem, row0 + kKRowStep * i, kvoff);
 #pragma unroll
-      for (int i = 0; i < kVTasks; ++i) {
-        const uint32_t voff = (uint32_t)vtask_row0(i) * rs + v_in_row;
+    for (int i = 0; i < kVTasks; ++i) {
+      const uint32_t voff = (uint32_t)vtask_row0(i) * rs + v_in_row;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pv[i][j] = vr.fast(kappa0 + j, voff);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kKChunks; ++i) pk[i] = kr.slow(kappa0, krow0 + kKRowStep * i, k_in_row, kend);
-#pragma unroll
-      for (int i = 0; i < kVTasks; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pv[i][j] = vr.slow(kappa0, vtask_row0(i) + j, v_in_row, kend);
+      for (int j = 0; j < 4; ++j) pv[i][j] = vr.load(mem, row0 + j, voff);
     }
   };
   auto lstore = [&](int buf) {
@@ -226,18 +221,20 @@ __global__ __launch_bounds__(NW * 64 * SPLIT, SPLIT == 1 && NW == 4 ? 2 : 1) voi
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
   float m = -INFINITY, l = 0.f;  // running max of the raw scores and this half's running sum
 
-  if (part < n_tiles) {
-    gload(part);
-    lstore(0);
-  }
+  // Loads and stores run unconditionally (clamped to the last tile; spare
+  // copies are never read): the wait before the first store then covers the
+  // query loads on every path, and the step loop carries one fixed set of
+  // loads in flight, so no wait in it has to drain them all.
+  gload(min(part, n_tiles - 1));
+  lstore(0);
   __syncthreads();
-  if (part + SPLIT < n_tiles) gload(part + SPLIT);
+  gload(min(part + SPLIT, n_tiles - 1));
 
   const int n_steps = (n_tiles + SPLIT - 1) / SPLIT;
   for (int step = 0; step < n_steps; ++step) {
     const int buf = step & 1;
     const int tile = SPLIT * step + part;
-    const int kappa0 = tile * kKT;
+    const int kappa0 = tile_kappa0(tile);
     if (tile < n_tiles) {
     // S^T for the tile's two 32-key blocks
     f32x16 s[2];
@@ -255,9 +252,11 @@ __global__ __launch_bounds__(NW * 64 * SPLIT, SPLIT == 1 && NW == 4 ? 2 : 1) voi
       for (int st = 0; st < 8; ++st) s[kb] = mfma32(kf[st], qf[st], s[kb]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // mask (only tiles that cross the causal limit), tile max of the raw scores
-    if (kappa0 + kKT > full_below) {
-      const int lim = causal0 + t + 1;
+    // mask (only the last memory tile when partial, and local tiles that cross
+    // the causal limit), tile max of the raw scores
+    const bool mem = tile_mem(tile);
+    if (mem ? kappa0 + kKT > mem_len : kappa0 + kKT > full_below) {
+      const int lim = mem ? mem_len : causal0 + t + 1;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -313,9 +312,9 @@ __global__ __launch_bounds__(NW * 64 * SPLIT, SPLIT == 1 && NW == 4 ? 2 : 1) voi
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (tile + SPLIT < n_tiles) lstore(buf ^ 1);
+    lstore(buf ^ 1);
     __syncthreads();
-    if (tile + 2 * SPLIT < n_tiles) gload(tile + 2 * SPLIT);
+    gload(min(tile + 2 * SPLIT, n_tiles - 1));
   }
 
   if constexpr (SPLIT == 2) {
