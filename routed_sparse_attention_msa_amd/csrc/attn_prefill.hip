@@ -17,9 +17,10 @@
 // bf16 -- no cross-lane traffic.  The key order inside each 32-key block is
 // chosen so that holds, and V is staged in LDS already in V^T operand order
 // (one 16-byte unit = the 8 keys one lane contributes to one MFMA, at one d),
-// so each V^T operand is a single 16-byte LDS read.  K tiles are stored in
-// an XOR-swizzled layout that keeps the operand reads free of bank
-// conflicts.  Each MFMA group's operand reads are issued before the group
+// so each V^T operand is a single 16-byte LDS read.  K rows sit at a padded
+// pitch that keeps the operand reads free of bank conflicts; every operand
+// read is a per-lane base plus a constant offset.  Each MFMA group's operand
+// reads are issued before the group
 // (one LDS latency per group, not per MFMA).  K and V rows are fetched with
 // buffer loads: a per-lane byte offset fixed for the whole kernel plus a
 // per-tile scalar offset and a scalar choice of the memory or local rows'
@@ -46,12 +47,13 @@ namespace {
 constexpr int kD = 128;
 constexpr int kKT = 64;                 // keys per LDS tile
 constexpr int kVGStride = 144;          // 16 B units per V group row: 128 d + one pad unit per 8
+constexpr int kKPitch = 272;            // bytes per K row in LDS: 256 + 16 pad (conflict-free reads)
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 struct PrefillSmem {
-  uint8_t k[2][kKT * 256];                // [key][256 B], 16 B segments XOR (key & 15)
+  uint8_t k[2][kKT * kKPitch];            // [key][256 B + pad]
   uint8_t v[2][8 * kVGStride * 16];       // [group][d + d/8][8 bf16]
 };
 
@@ -60,7 +62,6 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 }
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ int acc_row(int i, int hf) { return 8 * (i >> 2) + 4 * hf + (i & 3); }
-__device__ __forceinline__ int kswz(int key, int seg) { return key * 256 + ((seg ^ (key & 15)) << 4); }
 // V group G = 4*kb + 2*s2 + hf holds keys 32kb + 16s2 + 4hf + {0..3, 8..11} of the tile.
 __device__ __forceinline__ int vunit(int grp, int d) { return (grp * kVGStride + d + (d >> 3)) * 16; }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(NW * 64 * SPLIT, SPLIT == 1 && NW == 4 ? 2 : 1) voi
 #pragma unroll
     for (int i = 0; i < kKChunks; ++i) {
       const int c = tid + kThreads * i;
-      *reinterpret_cast<u32x4*>(&sm.k[buf][kswz(c >> 4, c & 15)]) = pk[i];
+      *reinterpret_cast<u32x4*>(&sm.k[buf][(c >> 4) * kKPitch + (c & 15) * 16]) = pk[i];
     }
 #pragma unroll
     for (int i = 0; i < kVTasks; ++i) {
@@ -236,16 +237,16 @@ __global__ __launch_bounds__(NW * 64 * SPLIT, SPLIT == 1 && NW == 4 ? 2 : 1) voi
     const int tile = SPLIT * step + part;
     const int kappa0 = tile_kappa0(tile);
     if (tile < n_tiles) {
-    // S^T for the tile's two 32-key blocks
+    // S^T for the tile's two 32-key blocks; lane (key cl, half hf) reads
+    // segments 8*(st/4) + 4*hf + st%4 of its key row
+    const uint8_t* kbase = &sm.k[buf][cl * kKPitch + hf * 64];
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       bf16x8 kf[8];
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const int seg = 8 * (st >> 2) + 4 * hf + (st & 3);
-        kf[st] = *reinterpret_cast<const bf16x8*>(&sm.k[buf][kswz(kb * 32 + cl, seg)]);
-      }
+      for (int st = 0; st < 8; ++st)
+        kf[st] = *reinterpret_cast<const bf16x8*>(kbase + kb * 32 * kKPitch + (8 * (st >> 2) + (st & 3)) * 16);
       __builtin_amdgcn_sched_barrier(0);
       s[kb] = f32x16{};
 #pragma unroll
@@ -263,17 +264,24 @@ __global__ __launch_bounds__(NW * 64 * SPLIT, SPLIT == 1 && NW == 4 ? 2 : 1) voi
         for (int i = 0; i < 16; ++i)
           if (kappa0 + kb * 32 + acc_row(i, hf) >= lim) s[kb][i] = -INFINITY;
     }
-    float mt = s[0][0];
+    // three-input max tree (v_max3): 16 instructions for the 32 scores
+    float mx[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kb][i]);
+    for (int j = 0; j < 4; ++j) {
+      const int kb = j >> 1, i0 = 8 * (j & 1);
+      float a = fmaxf(fmaxf(s[kb][i0], s[kb][i0 + 1]), s[kb][i0 + 2]);
+      a = fmaxf(fmaxf(a, s[kb][i0 + 3]), s[kb][i0 + 4]);
+      a = fmaxf(fmaxf(a, s[kb][i0 + 5]), s[kb][i0 + 6]);
+      mx[j] = fmaxf(a, s[kb][i0 + 7]);
+    }
+    float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float m_new = fmaxf(m, mt);
     const float alpha = fast_exp2((m - m_new) * scale_log2);
     m = m_new;
     const float off = -m_new * scale_log2;
-    float lsum = 0.f;
+    // probabilities (float32 row sum, two chains), rounded to bf16 for PV
+    float lsum2[2] = {0.f, 0.f};
     bf16x8 pf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -284,28 +292,29 @@ __global__ __launch_bounds__(NW * 64 * SPLIT, SPLIT == 1 && NW == 4 ? 2 : 1) voi
         for (int e = 0; e < 4; ++e) {
           const float p0 = fast_exp2(fmaf(s[kb][8 * s2 + 2 * e], scale_log2, off));
           const float p1 = fast_exp2(fmaf(s[kb][8 * s2 + 2 * e + 1], scale_log2, off));
-          lsum += p0 + p1;
+          lsum2[s2] += p0 + p1;
           w[e] = pack_bf16x2(p0, p1);
         }
         pf[kb][s2] = as_bf16x8(w);
       }
-    l = l * alpha + lsum;
+    l = l * alpha + (lsum2[0] + lsum2[1]);
     if (__any(alpha != 1.f)) {
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
     }
-    // O^T += V^T P^T: lane (d, hf) reads its 8 keys of group 4kb + 2s2 + hf at column d.
+    // O^T += V^T P^T: lane (d, hf) reads its 8 keys of group 4kb + 2s2 + hf at
+    // column d = 32db + cl, i.e. unit vunit(grp, d) = lane base + a constant.
+    const uint8_t* vbase = &sm.v[buf][(hf * kVGStride + cl + (cl >> 3)) * 16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        const int grp = 4 * kb + 2 * s2 + hf;
         bf16x8 vf[4];
 #pragma unroll
         for (int db = 0; db < 4; ++db)
-          vf[db] = *reinterpret_cast<const bf16x8*>(&sm.v[buf][vunit(grp, db * 32 + cl)]);
+          vf[db] = *reinterpret_cast<const bf16x8*>(vbase + ((4 * kb + 2 * s2) * kVGStride + 36 * db) * 16);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int db = 0; db < 4; ++db) o[db] = mfma32(vf[db], pf[kb][s2], o[db]);
