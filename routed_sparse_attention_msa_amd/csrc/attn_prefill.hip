@@ -51,6 +51,7 @@ constexpr int kKPitch = 272;            // bytes per K row in LDS: 256 + 16 pad 
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.f;  // log2 headroom of the lazy running max
 
 struct PrefillSmem {
   uint8_t k[2][kKT * kKPitch];            // [key][256 B + pad]
@@ -221,6 +222,7 @@ __global__ __launch_bounds__(NW * 64 * SPLIT, SPLIT == 1 && NW == 4 ? 2 : 1) voi
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
   float m = -INFINITY, l = 0.f;  // running max of the raw scores and this half's running sum
+  const float lazy = kLazy / scale_log2;
 
   // Loads and stores run unconditionally (clamped to the last tile; spare
   // copies are never read): the wait before the first store then covers the
@@ -276,10 +278,15 @@ __global__ __launch_bounds__(NW * 64 * SPLIT, SPLIT == 1 && NW == 4 ? 2 : 1) voi
     }
     float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m, mt);
-    const float alpha = fast_exp2((m - m_new) * scale_log2);
+    // Lazy running max: it moves only when a score exceeds it by more than
+    // kLazy / scale_log2 (probabilities then stay <= 2^kLazy, harmless in
+    // float32), so the O^T rescale below is rare after the first tiles.
+    // (While a lane has seen no visible key, m stays -inf: alpha is then 1
+    // and the exponent offset 0, so masked scores give 0, never NaN.)
+    const float m_new = mt > m + lazy ? mt : m;
+    const float alpha = m_new == m ? 1.f : fast_exp2((m - m_new) * scale_log2);
     m = m_new;
-    const float off = -m_new * scale_log2;
+    const float off = m_new == -INFINITY ? 0.f : -m_new * scale_log2;
     // probabilities (float32 row sum, two chains), rounded to bf16 for PV
     float lsum2[2] = {0.f, 0.f};
     bf16x8 pf[2][2];

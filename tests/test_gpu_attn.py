@@ -58,6 +58,8 @@ def _check(q, ks, vs, kl, vl, rtol, lse_atol):
     (1, 16, 2, 1, 64, 16, 20, torch.bfloat16),         # head dim 64
     (1, 9, 2, 2, 96, 5, 9, torch.float32),             # odd head dim
     (1, 64, 4, 2, 128, 32, 64, torch.bfloat16),        # group size 2
+    (1, 64, 4, 1, 128, 0, 100, torch.bfloat16),        # a key half whose first tile is past the
+    (1, 40, 8, 2, 128, 0, 90, torch.bfloat16),         #   first queries' causal limit (all masked)
     (32, 1, 32, 8, 128, 32, 250, torch.bfloat16),      # decode, one workgroup per (sequence, KV head)
     (40, 2, 16, 8, 128, 16, 90, torch.bfloat16),       # more pairs than CUs, 2 tokens
     (1, 1, 8, 1, 128, 64, 5000, torch.bfloat16),       # one pair: many runs of splits, combined
