@@ -582,18 +582,29 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
   }
 
   // --- staging: 4 x 16 B of q and 4 x 16 B of k per thread per stage ----------
+  // Buffer loads: a per-lane offset fixed for the kernel plus the stage's
+  // scalar offset; rows past t_tot / n_ch lie beyond the resources' records
+  // and read as zeros, so the loads carry no branches and no address math.
+  const uint32_t row_bytes = (uint32_t)(row_elems * 2);
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(q_r + (size_t)row0 * row_elems), 0,
+      (int)((size_t)max(0, min(kTB, t_tot - row0)) * row_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(kbar + (size_t)col0 * row_elems), 0,
+      (int)((size_t)max<int64_t>(0, min<int64_t>(kNB, n_ch - col0)) * row_bytes), 0x00020000);
+  uint32_t voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + kTiledThreads * i;
+    voff[i] = (uint32_t)(c >> 3) * row_bytes + (c & 7) * 16;
+  }
   u32x4 pq[4], pk[4];
   auto gload = [&](int stage) {
-    const int h = stage >> 1, half = stage & 1;
+    const uint32_t soff = (uint32_t)((stage >> 1) * kDim + (stage & 1) * 64) * 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = tid + kTiledThreads * i;
-      const int r = c >> 3, seg = c & 7;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      const int qr = row0 + r;
-      pq[i] = qr < t_tot ? load16(q_r + (size_t)qr * row_elems + h * kDim + half * 64 + seg * 8) : z;
-      const int64_t kn = col0 + r;
-      pk[i] = kn < n_ch ? load16(kbar + (size_t)kn * row_elems + h * kDim + half * 64 + seg * 8) : z;
+      pq[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, voff[i], soff, 0));
+      pk[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, voff[i], soff, 0));
     }
   };
   auto lstore = [&](int buf) {
@@ -612,14 +623,24 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
 
-  const int n_stages = 2 * heads;
-  gload(0);
-  lstore(0);
-  if (n_stages > 1) gload(1);
-  __syncthreads();
-
-  for (int st = 0; st < n_stages; ++st) {
-    const int buf = st & 1;
+  // chain to head hn (or, with hn == heads, apply the final scale)
+  auto rescale = [&](int hn) {
+    float ck[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) ck[b] = sm.rk[hn][wn * 64 + b * 32 + cl];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 rq4 = *reinterpret_cast<const f32x4*>(&sm.rq[hn][wm * 128 + a * 32 + 8 * q + 4 * hf]);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[a][b][4 * q + e] *= rq4[e] * ck[b];
+      }
+    }
+  };
+  auto stage_mfma = [&](int buf) {
     const uint8_t* qs = sm.q[buf];
     const uint8_t* ks = sm.k[buf];
 #pragma unroll
@@ -641,28 +662,29 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[a][b] = mfma32(af[a], bfr[b], acc[a][b]);
     }
-    if (st + 1 < n_stages) lstore(buf ^ 1);
-    if (st + 2 < n_stages) gload(st + 2);
+  };
+
+  // Two stages (the halves of one head) per iteration; the previous head's
+  // chained rescale opens the iteration, in the same block as this head's
+  // MFMAs, so it can overlap them.  Loads are issued unconditionally
+  // (clamped to the last stage) so one fixed set is in flight.
+  const int n_stages = 2 * heads;
+  gload(0);
+  lstore(0);
+  gload(1);
+  __syncthreads();
+  for (int h = 0; h < heads; ++h) {
+    if (h > 0) rescale(h);
+    stage_mfma(0);
+    lstore(1);
+    gload(min(2 * h + 2, n_stages - 1));
     __syncthreads();
-    if (st & 1) {
-      // head h = st/2 finished: chain to head h+1, or apply the final scale
-      const int hn = (st >> 1) + 1;
-      float ck[2];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) ck[b] = sm.rk[hn][wn * 64 + b * 32 + cl];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 rq4 = *reinterpret_cast<const f32x4*>(&sm.rq[hn][wm * 128 + a * 32 + 8 * q + 4 * hf]);
-#pragma unroll
-          for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[a][b][4 * q + e] *= rq4[e] * ck[b];
-        }
-      }
-    }
+    stage_mfma(1);
+    lstore(0);
+    gload(min(2 * h + 3, n_stages - 1));
+    __syncthreads();
   }
+  rescale(heads);
 
   // --- epilogue: max over each row block's 32 rows, then each doc's chunks ----
   const int ndw = kNB / cpd;  // documents per workgroup tile
