@@ -25,17 +25,18 @@
 // (queries) and B (keys) use the same order, so each step still pairs
 // matching elements; only the float32 summation order changes.
 //
-// Two kernels:
-//  * route_stream  (few query rows): one workgroup owns 32 pooled chunks;
-//    each wave owns two heads, keeps their key fragments in registers
-//    (loaded straight from HBM with 16-byte loads, read exactly once), and
-//    loops over 32-row query tiles; the waves' head partials meet in LDS.
-//    HBM-bound: the bank streams once whatever the query count.
+// Three kernels:
+//  * route_scan    (up to 128 query rows, 2/4/8 heads): persistent workgroups
+//    stream the bank once through LDS, tile by tile; the HBM-bound case.
+//  * route_stream  (other few-row shapes): one workgroup owns 32 pooled
+//    chunks; each wave owns two heads, keeps their key fragments in registers
+//    (loaded straight from HBM, read exactly once), and loops over 32-row
+//    query tiles; the waves' head partials meet in LDS.
 //  * route_tiled   (many query rows): 256x256 output tile per workgroup,
 //    8 waves (2 x 4), each wave 128 rows x 64 columns (4 x 2 MFMA blocks);
 //    query and key slices are staged through XOR-swizzled, double-buffered
 //    LDS, 64 k-elements of one head per stage.  MFMA-bound.
-// Both end with the max over each document's chunks (cross-lane shuffles)
+// All end with the max over each document's chunks (cross-lane shuffles)
 // and over the query tokens of each sequence.
 #include <algorithm>
 
