@@ -28,6 +28,9 @@ from .msa_oracle import (
     pool_chunks_mean,
     pool_chunks_stored,
     chunk_norms,
+    rope_rotate_half,
+    chunk_offsets,
+    encode_docs,
     route_scores,
     topk_docs,
     gather_kv,
@@ -43,6 +46,9 @@ __all__ = [
     "pool_chunks_mean",
     "pool_chunks_stored",
     "chunk_norms",
+    "rope_rotate_half",
+    "chunk_offsets",
+    "encode_docs",
     "route_scores",
     "topk_docs",
     "gather_kv",

@@ -92,6 +92,74 @@ def chunk_norms(xbar_stored):
 
 
 # ---------------------------------------------------------------------------
+# Offline encoder over variable-length documents (S1 at scale)
+# ---------------------------------------------------------------------------
+
+def rope_rotate_half(x, positions, base):
+    """Rotary position embedding, rotate-half form, in float64.
+
+    ``x`` [L, H, d] (d even), ``positions`` [L].  For k < d/2 the pair
+    (x_k, x_{k+d/2}) is rotated by the angle positions * theta_k with
+    theta_k = base ** (-2k / d):
+        x'_k       = x_k cos - x_{k+d/2} sin
+        x'_{k+d/2} = x_{k+d/2} cos + x_k sin
+
+    Reading ([README] "Overall Design"; [Card] "Architecture summary"): the
+    pages name document-wise RoPE but neither its form nor its base; the
+    rotate-half form with base 1e6 is a Qwen-like assumption, and only K is
+    rotated (V and the router key K_r are not).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    if d % 2:
+        raise ValueError("rotary embedding needs an even head dim")
+    half = d // 2
+    theta = np.power(float(base), -2.0 * np.arange(half) / d)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * theta[None, :]   # [L, half]
+    cos, sin = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1)
+
+
+def chunk_offsets(doc_off, chunk):
+    """First pooled chunk of each document: chunk_off[n] = sum_{m<n} ceil(L_m / chunk)."""
+    doc_off = np.asarray(doc_off, dtype=np.int64)
+    lens = np.diff(doc_off)
+    if np.any(lens < 0) or doc_off[0] != 0:
+        raise ValueError("doc_off must start at 0 and be nondecreasing")
+    n_ch = (lens + chunk - 1) // chunk
+    return np.concatenate([[0], np.cumsum(n_ch)]).astype(np.int64)
+
+
+def encode_docs(x, doc_off, chunk, rope_base=None):
+    """Chunk means of variable-length documents, optionally after document-wise RoPE.
+
+    ``x`` [total_rows, H, d]; document n is rows doc_off[n] .. doc_off[n+1]-1.
+    Chunk j of document n is the mean of its rows j*chunk .. min((j+1)*chunk,
+    L_n) - 1 -- the last chunk of a document may be shorter, and its mean is
+    over the rows present.  With ``rope_base`` the rows are first rotated at
+    their document-local positions 0 .. L_n - 1 (rope_rotate_half).  Returns
+    the exact float64 means [total_chunks, H, d] and chunk_offsets.
+
+    Follows [README] "Overall Design" (chunk-mean compression) and "Inference
+    Pipeline" stage 1 (offline encoding of the memory).  Reading: the pages
+    never show a partial last chunk; the mean over the rows present is the
+    plainest reading of a chunk mean.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    c_off = chunk_offsets(doc_off, chunk)
+    out = np.empty((int(c_off[-1]),) + x.shape[1:], dtype=np.float64)
+    for n in range(len(doc_off) - 1):
+        rows = x[doc_off[n]:doc_off[n + 1]]
+        if rope_base is not None and len(rows):
+            rows = rope_rotate_half(rows, np.arange(len(rows)), rope_base)
+        for j in range(int(c_off[n + 1] - c_off[n])):
+            seg = rows[j * chunk:(j + 1) * chunk]
+            out[c_off[n] + j] = seg.sum(axis=0) / len(seg)
+    return out, c_off
+
+
+# ---------------------------------------------------------------------------
 # S2: cosine routing
 # ---------------------------------------------------------------------------
 
