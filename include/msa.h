@@ -84,6 +84,42 @@ msa_status msa_pool_chunks(const void* x, void* xbar, float* xbar_norm, int64_t 
                            msa_dtype dt, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Offline encoder over variable-length documents (MSA README "Overall
+ * Design": chunk-mean compression of document K, V and K_r, K rotated by
+ * document-wise RoPE; "Inference Pipeline", stage 1: offline encoding).
+ *
+ * Documents are row ranges of one tensor: document n is rows
+ * doc_off[n] .. doc_off[n+1]-1.  Each is cut into chunks of `chunk` rows; the
+ * last chunk of a document may be shorter and its mean is over the rows
+ * present (a reading: the pages never show one).
+ *
+ * msa_chunk_offsets: chunk_off[0] = 0,
+ *   chunk_off[n+1] = chunk_off[n] + ceil((doc_off[n+1] - doc_off[n]) / chunk).
+ *   doc_off, chunk_off: device int64 arrays of n_docs + 1 entries.  doc_off
+ *   must start at 0 and be nondecreasing (not checked on the device).
+ *
+ * msa_encode_docs:
+ *   xbar[chunk_off[n] + j, h, :] = (1/cnt) * sum_{i<cnt} R(j*chunk + i) x[doc_off[n] + j*chunk + i, h, :]
+ *   with cnt = min(chunk, L_n - j*chunk) and R(p) the identity when
+ *   rope_base == 0, else the rotate-half rotary embedding at position p: for
+ *   k < dim/2 the pair (x_k, x_{k+dim/2}) turns by p * rope_base^(-2k/dim).
+ *   x          [total_rows, heads, dim]          input rows (dtype dt)
+ *   xbar       [total_chunks, heads, dim]        output (dtype dt), total_chunks = chunk_off[n_docs]
+ *   xbar_norm  [total_chunks, heads] float32, or NULL: norms of the stored rows
+ *   doc_off, chunk_off: as above (chunk_off from msa_chunk_offsets).
+ *   Requires heads*dim*sizeof(dt) % 16 == 0; with xbar_norm or rope_base > 0,
+ *   dim*sizeof(dt) must be a power of two in [32, 1024].  Offsets that point
+ *   outside x read nothing (the chunk comes out as zeros); they are not
+ *   reported.  rope_base == 0 and equal lengths reproduce msa_pool_chunks.
+ * ---------------------------------------------------------------------- */
+msa_status msa_chunk_offsets(const int64_t* doc_off, int64_t n_docs, int32_t chunk,
+                             int64_t* chunk_off, void* stream);
+msa_status msa_encode_docs(const void* x, void* xbar, float* xbar_norm, const int64_t* doc_off,
+                           const int64_t* chunk_off, int64_t n_docs, int64_t total_rows,
+                           int64_t total_chunks, int32_t chunk, int32_t heads, int32_t dim,
+                           float rope_base, msa_dtype dt, void* stream);
+
+/* ------------------------------------------------------------------------
  * S2  Cosine routing scores (MSA README "Overall Design": cosine similarity
  *     averaged over heads, then maximised over query tokens; model card
  *     opening paragraph: per-layer router over the chunk-pooled bank).

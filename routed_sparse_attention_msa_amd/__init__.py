@@ -4,6 +4,8 @@ The work runs in hand-written HIP kernels in ``libmsa.so`` behind the C ABI
 of ``include/msa.h``; this package is its thin Python binding:
 
     msa_pool_chunks    S1  chunk-mean pooling of K / V / K_r into the bank
+    msa_chunk_offsets  \   offline encoder over variable-length documents:
+    msa_encode_docs    /   document-wise RoPE + chunk means (+ norms)
     msa_route_scores   S2  cosine routing scores per document
     msa_topk_docs      S3  top-k documents
     msa_gather_kv      S4  gather (or host-tier fetch) of the selected pooled K/V
@@ -14,6 +16,8 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     MsaError,
     lib,
+    msa_chunk_offsets,
+    msa_encode_docs,
     msa_gather_kv,
     msa_pool_chunks,
     msa_route_scores,

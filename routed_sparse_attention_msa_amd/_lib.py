@@ -28,6 +28,9 @@ SIGNATURES = {
     "msa_last_error": (ctypes.c_char_p, []),
     "msa_pool_chunks": (_STATUS, [c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_int32, c_int32,
                                   c_int32, c_int, c_void_p]),
+    "msa_chunk_offsets": (_STATUS, [c_void_p, c_int64, c_int32, c_void_p, c_void_p]),
+    "msa_encode_docs": (_STATUS, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int64,
+                                  c_int64, c_int32, c_int32, c_int32, c_float, c_int, c_void_p]),
     "msa_route_scores_workspace": (_STATUS, [c_int32, c_int32, c_int32, c_int32, c_int64, c_int32,
                                              c_int, POINTER(c_size_t)]),
     "msa_route_scores": (_STATUS, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
@@ -140,6 +143,53 @@ def msa_pool_chunks(x, chunk, xbar=None, xbar_norm=None, with_norm=False):
             raise ValueError(f"xbar_norm must be {(n_ch, heads)}")
     _check(lib().msa_pool_chunks(_ptr(x), _ptr(xbar), _ptr(xbar_norm), n_docs, doc_len, chunk, heads,
                                  dim, _dtype_code(x), _stream(x.device)))
+    return xbar, xbar_norm
+
+
+def msa_chunk_offsets(doc_off, chunk, chunk_off=None):
+    """First pooled chunk of each document (device int64 [n_docs + 1]) from the
+    document row offsets ``doc_off`` (device int64 [n_docs + 1])."""
+    _dev(doc_off, "doc_off", dtype=torch.int64, ndim=1)
+    n_docs = doc_off.numel() - 1
+    if n_docs < 0:
+        raise ValueError("doc_off needs n_docs + 1 >= 1 entries")
+    if chunk_off is None:
+        chunk_off = torch.empty_like(doc_off)
+    _dev(chunk_off, "chunk_off", dtype=torch.int64, ndim=1)
+    if chunk_off.numel() != n_docs + 1:
+        raise ValueError("chunk_off must have n_docs + 1 entries")
+    _check(lib().msa_chunk_offsets(_ptr(doc_off), n_docs, chunk, _ptr(chunk_off), _stream(doc_off.device)))
+    return chunk_off
+
+
+def msa_encode_docs(x, doc_off, chunk_off, total_chunks, chunk, rope_base=0.0, xbar=None,
+                    xbar_norm=None, with_norm=False):
+    """Chunk means of variable-length documents: ``x`` [total_rows, heads, dim]
+    with document n at rows doc_off[n] .. doc_off[n+1]-1, optionally rotated by
+    document-wise RoPE (``rope_base`` > 0) first.  ``total_chunks`` must equal
+    chunk_off[-1] (known on the host from the document lengths).  Returns
+    (xbar [total_chunks, heads, dim], xbar_norm [total_chunks, heads] or None)."""
+    _dev(x, "x", ndim=3)
+    _dev(doc_off, "doc_off", dtype=torch.int64, ndim=1)
+    _dev(chunk_off, "chunk_off", dtype=torch.int64, ndim=1)
+    total_rows, heads, dim = x.shape
+    n_docs = doc_off.numel() - 1
+    if chunk_off.numel() != n_docs + 1:
+        raise ValueError("chunk_off must have as many entries as doc_off")
+    if xbar is None:
+        xbar = torch.empty((total_chunks, heads, dim), dtype=x.dtype, device=x.device)
+    _dev(xbar, "xbar", dtype=x.dtype)
+    if xbar.shape != (total_chunks, heads, dim):
+        raise ValueError(f"xbar must be {(total_chunks, heads, dim)}")
+    if with_norm and xbar_norm is None:
+        xbar_norm = torch.empty((total_chunks, heads), dtype=torch.float32, device=x.device)
+    if xbar_norm is not None:
+        _dev(xbar_norm, "xbar_norm", dtype=torch.float32)
+        if xbar_norm.shape != (total_chunks, heads):
+            raise ValueError(f"xbar_norm must be {(total_chunks, heads)}")
+    _check(lib().msa_encode_docs(_ptr(x), _ptr(xbar), _ptr(xbar_norm), _ptr(doc_off), _ptr(chunk_off),
+                                 n_docs, total_rows, total_chunks, chunk, heads, dim, float(rope_base),
+                                 _dtype_code(x), _stream(x.device)))
     return xbar, xbar_norm
 
 

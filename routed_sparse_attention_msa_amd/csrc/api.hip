@@ -125,6 +125,46 @@ msa_status msa_pool_chunks(const void* x, void* xbar, float* xbar_norm, int64_t 
 }
 
 // ---------------------------------------------------------------------------
+msa_status msa_chunk_offsets(const int64_t* doc_off, int64_t n_docs, int32_t chunk,
+                             int64_t* chunk_off, void* stream) {
+  CHECK_ARG(n_docs >= 0 && chunk > 0, "n_docs must be >= 0 and chunk > 0 (n_docs=%lld chunk=%d)",
+            (long long)n_docs, chunk);
+  CHECK_ARG(doc_off && chunk_off, "null pointer");
+  CHECK_ARG(((uintptr_t)doc_off & 7u) == 0 && ((uintptr_t)chunk_off & 7u) == 0, "offsets misaligned");
+  return hip_status(msa::launch_chunk_offsets(doc_off, n_docs, chunk, chunk_off,
+                                              static_cast<hipStream_t>(stream)),
+                    "msa_chunk_offsets launch");
+}
+
+msa_status msa_encode_docs(const void* x, void* xbar, float* xbar_norm, const int64_t* doc_off,
+                           const int64_t* chunk_off, int64_t n_docs, int64_t total_rows,
+                           int64_t total_chunks, int32_t chunk, int32_t heads, int32_t dim,
+                           float rope_base, msa_dtype dt, void* stream) {
+  CHECK_ARG(valid_dtype(dt), "unknown dtype %d", (int)dt);
+  CHECK_ARG(n_docs >= 0 && total_rows >= 0 && total_chunks >= 0 && chunk > 0 && heads > 0 && dim > 0,
+            "sizes must be positive (n_docs=%lld total_rows=%lld total_chunks=%lld chunk=%d heads=%d dim=%d)",
+            (long long)n_docs, (long long)total_rows, (long long)total_chunks, chunk, heads, dim);
+  CHECK_ARG(rope_base >= 0.f && rope_base == rope_base, "rope_base must be >= 0 (0: no rotation)");
+  const size_t es = dtype_size(dt);
+  CHECK_ARG(((size_t)heads * dim * es) % 16 == 0, "heads*dim*sizeof(dtype) must be a multiple of 16");
+  if (xbar_norm != nullptr || rope_base > 0.f) {
+    const int64_t hb = (int64_t)dim * (int64_t)es;
+    CHECK_ARG(is_pow2(hb) && hb >= 32 && hb <= 1024,
+              "with norms or RoPE, dim*sizeof(dtype) must be a power of two in [32, 1024] (got %lld)",
+              (long long)hb);
+  }
+  CHECK_ARG(xbar_norm == nullptr || ((uintptr_t)xbar_norm & 3u) == 0, "xbar_norm misaligned");
+  if (n_docs == 0 || total_chunks == 0) return MSA_OK;
+  CHECK_ARG(x && xbar && doc_off && chunk_off, "null pointer");
+  CHECK_ARG(aligned16(x) && aligned16(xbar), "x and xbar must be 16-byte aligned");
+  CHECK_ARG(((uintptr_t)doc_off & 7u) == 0 && ((uintptr_t)chunk_off & 7u) == 0, "offsets misaligned");
+  return hip_status(msa::launch_encode(x, xbar, xbar_norm, doc_off, chunk_off, n_docs, total_rows,
+                                       total_chunks, chunk, heads, dim, rope_base, dt,
+                                       static_cast<hipStream_t>(stream)),
+                    "msa_encode_docs launch");
+}
+
+// ---------------------------------------------------------------------------
 static msa_status check_route(int32_t batch, int32_t q_len, int32_t heads, int32_t dim,
                               int64_t n_docs, int32_t cpd, msa_dtype dt) {
   CHECK_ARG(valid_dtype(dt), "unknown dtype %d", (int)dt);

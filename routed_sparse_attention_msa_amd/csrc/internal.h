@@ -99,6 +99,13 @@ inline int device_cu_count() {
 hipError_t launch_pool(const void* x, void* xbar, float* norm, int64_t n_chunks, int chunk,
                        int heads, int dim, msa_dtype dt, hipStream_t s);
 
+hipError_t launch_chunk_offsets(const int64_t* doc_off, int64_t n_docs, int chunk, int64_t* chunk_off,
+                                hipStream_t s);
+hipError_t launch_encode(const void* x, void* xbar, float* norm, const int64_t* doc_off,
+                         const int64_t* chunk_off, int64_t n_docs, int64_t total_rows,
+                         int64_t total_chunks, int chunk, int heads, int dim, float rope_base,
+                         msa_dtype dt, hipStream_t s);
+
 size_t route_workspace_bytes(int batch, int q_len, int heads, int dim, int64_t n_docs, int cpd,
                              msa_dtype dt);
 hipError_t launch_route(const void* q_r, const void* kbar_r, const float* knorm, int batch,

@@ -63,6 +63,25 @@ def test_pool_validation():
     assert lib.msa_pool_chunks(None, None, None, 0, 512, 64, 8, 128, L.MSA_BF16, None) == L.MSA_OK
 
 
+def test_encode_validation():
+    lib = msa.lib()
+    p = ctypes.c_void_p(16)
+    # chunk must be positive
+    assert lib.msa_chunk_offsets(p, 4, 0, p, None) == L.MSA_ERR_INVALID
+    assert lib.msa_encode_docs(p, p, None, p, p, 4, 100, 10, 0, 8, 128, 0.0, L.MSA_BF16, None) == L.MSA_ERR_INVALID
+    # RoPE needs a power-of-two head of at least 32 bytes
+    assert lib.msa_encode_docs(p, p, None, p, p, 4, 100, 10, 8, 2, 8, 1e4, L.MSA_BF16, None) == L.MSA_ERR_INVALID
+    assert "power of two" in _err()
+    assert lib.msa_encode_docs(p, p, None, p, p, 4, 100, 10, 8, 1, 24, 1e4, L.MSA_BF16, None) == L.MSA_ERR_INVALID
+    # negative rope base, unknown dtype, misaligned rows
+    assert lib.msa_encode_docs(p, p, None, p, p, 4, 100, 10, 8, 8, 128, -1.0, L.MSA_BF16, None) == L.MSA_ERR_INVALID
+    assert lib.msa_encode_docs(p, p, None, p, p, 4, 100, 10, 8, 8, 128, 0.0, 9, None) == L.MSA_ERR_INVALID
+    q = ctypes.c_void_p(18)
+    assert lib.msa_encode_docs(q, p, None, p, p, 4, 100, 10, 8, 8, 128, 0.0, L.MSA_BF16, None) == L.MSA_ERR_INVALID
+    # no chunks is a no-op
+    assert lib.msa_encode_docs(None, None, None, None, None, 0, 0, 0, 8, 8, 128, 0.0, L.MSA_BF16, None) == L.MSA_OK
+
+
 def test_topk_validation_and_workspace():
     lib = msa.lib()
     n = ctypes.c_size_t(123)
