@@ -1,6 +1,6 @@
 """Benchmark of the MSA routed-layer hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode|encode] [--no-cpu-baseline]
 
 A step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM:
@@ -11,6 +11,9 @@ already resident in HBM:
   decode  (the same bank; 32 sequences x 1 token, 4096 cached tokens, top-16):
       route -> top-k -> gather -> split-KV attention (the bank is pooled once,
       outside the timed region, as the offline stage of the pipeline)
+  encode  (offline encoder: 2048 documents of 256..768 tokens, ~1M tokens,
+           8 KV heads x 128, bf16): chunk offsets -> encode K (document-wise
+           RoPE, base 1e6) -> encode V -> encode K_r (+ norms)
 
 Prints one JSON line.  `value` is query tokens per second of the whole step.
 Per-kernel durations are measured with HIP events on the stream the kernels
@@ -52,7 +55,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", choices=["prefill", "decode"], default="prefill")
+    p.add_argument("--workload", choices=["prefill", "decode", "encode"], default="prefill")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     # profiling helpers (see "Profiles" in the module docstring)
@@ -135,6 +138,8 @@ STAGE_KERNELS = {
                 "attn": ("attn_prefill", "attn_prefill.hip")},
     "decode": {"route": ("route_", "route.hip"), "topk": ("topk", "topk.hip"),
                "gather": ("gather", "gather.hip"), "attn": ("attn_decode", "attn_decode.hip")},
+    "encode": {"offsets": ("chunk_offsets", "encode.hip"), "encode": ("encode_kernel", "encode.hip")},
+    # (both encode launches share one kernel template; the traffic entry covers their average)
 }
 COPY_PROBE_BYTES = 1 << 30
 
@@ -342,6 +347,124 @@ class Step:
         return marks
 
 
+class EncodeStep:
+    """Offline encoder over variable-length documents: the seeded recipe draws
+    2048 lengths uniform in [256, 768] (about 1M tokens) and N(0,1)/sqrt(128)
+    bf16 rows for K, V and K_r; K is rotated at document-local positions."""
+
+    N_DOCS, LEN_LO, LEN_HI, HEADS, DIM, CHUNK, ROPE_BASE = 2048, 256, 768, 8, 128, 64, 1.0e6
+
+    def __init__(self, seed, dev):
+        import numpy as np
+        import torch
+        import routed_sparse_attention_msa_amd as msa
+        self.torch, self.msa = torch, msa
+        rng = np.random.default_rng(seed)
+        lens = rng.integers(self.LEN_LO, self.LEN_HI + 1, self.N_DOCS)
+        self.doc_off_h = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+        self.rows = int(self.doc_off_h[-1])
+        self.chunks = int(((lens + self.CHUNK - 1) // self.CHUNK).sum())
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        mk = lambda: (torch.randn((self.rows, self.HEADS, self.DIM), generator=g, device=dev)
+                      / math.sqrt(self.DIM)).to(torch.bfloat16)
+        self.k, self.v, self.k_r = mk(), mk(), mk()
+        self.doc_off = torch.as_tensor(self.doc_off_h, device=dev)
+        self.chunk_off = torch.empty_like(self.doc_off)
+        e = lambda: torch.empty((self.chunks, self.HEADS, self.DIM), dtype=torch.bfloat16, device=dev)
+        self.kbar, self.vbar, self.kbar_r = e(), e(), e()
+        self.knorm = torch.empty((self.chunks, self.HEADS), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+
+    def calls(self):
+        msa, c = self.msa, self.CHUNK
+        enc = lambda x, out, rope, norm: msa.msa_encode_docs(x, self.doc_off, self.chunk_off, self.chunks, c,
+                                                             rope_base=rope, xbar=out, xbar_norm=norm)
+        return [("offsets", lambda: msa.msa_chunk_offsets(self.doc_off, c, chunk_off=self.chunk_off)),
+                ("encode_rope", lambda: enc(self.k, self.kbar, self.ROPE_BASE, None)),
+                ("encode", lambda: enc(self.v, self.vbar, 0.0, None)),
+                ("encode", lambda: enc(self.k_r, self.kbar_r, 0.0, self.knorm))]
+
+    run = Step.run
+
+    def work(self, stage):
+        rb = self.HEADS * self.DIM * 2
+        if stage == "offsets":
+            return {"bound": "hbm", "bytes": 2 * 8 * (self.N_DOCS + 1), "flops": 0}
+        # K (rotated) alone; V and K_r (+ norms) averaged
+        b = self.rows * rb + self.chunks * rb + (0 if stage == "encode_rope" else self.chunks * self.HEADS * 2)
+        return {"bound": "hbm", "bytes": b, "flops": self.rows * self.HEADS * self.DIM}
+
+    def cpu_baseline(self):
+        from oracle import encode_docs
+        try:
+            from threadpoolctl import threadpool_info
+            blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:  # pragma: no cover
+            blas = 1
+        # every document: about 10 s of float64 work on the host
+        docs = range(self.N_DOCS)
+        secs, rows = 0.0, 0
+        for n in docs:
+            a, b = int(self.doc_off_h[n]), int(self.doc_off_h[n + 1])
+            rows += b - a
+            for x, rope in ((self.k, self.ROPE_BASE), (self.v, None), (self.k_r, None)):
+                xs = x[a:b].float().cpu().double().numpy()
+                t0 = time.perf_counter()
+                encode_docs(xs, [0, b - a], self.CHUNK, rope)
+                secs += time.perf_counter() - t0
+        return {"value": rows / secs, "unit": "encoded tokens/s", "cores": int(blas), "kind": "oracle",
+                "sample": f"the whole step: {self.N_DOCS} documents ({rows} rows) x 3 tensors",
+                "seconds_per_step": secs}
+
+
+def main_encode(args):
+    import torch
+    dev = "cuda:0"
+    print("[bench] building inputs for encode-1M-varlen-bf16", file=sys.stderr, flush=True)
+    step = EncodeStep(args.seed, dev)
+    step.run(args.warmup, events=False)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    marks = step.run(args.steps, events=True)
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    per, counts = {}, {}
+    for stage, a, b in marks:
+        per[stage] = per.get(stage, 0.0) + a.elapsed_time(b)
+        counts[stage] = counts.get(stage, 0) + 1
+    stages = {}
+    for stage in per:
+        avg = per[stage] / counts[stage]
+        entry = roofline_entry(step.work(stage), avg)
+        entry.update({"avg_launch_ms": avg, "launches_per_step": counts[stage] // args.steps,
+                      "ms_per_step": per[stage] / args.steps})
+        stages[stage] = entry
+    dom = max(stages, key=lambda k: stages[k]["ms_per_step"])
+    roof = {k: stages[dom][k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+    roof.update({"kernel": dom, "avg_launch_ms": stages[dom]["avg_launch_ms"],
+                 "traffic": measured_traffic("encode", dom)})
+    rec = {
+        "metric": "encoded document tokens/s (offline encoder, variable-length documents)",
+        "value": step.rows / (ms_per_step / 1e3), "unit": "encoded tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "encode-1M-varlen-bf16", "n_docs": step.N_DOCS,
+                   "doc_len_range": [step.LEN_LO, step.LEN_HI], "total_rows": step.rows,
+                   "total_chunks": step.chunks, "chunk": step.CHUNK, "heads_kv": step.HEADS, "dim": step.DIM,
+                   "rope_base": step.ROPE_BASE,
+                   "step": "chunk offsets -> encode K (RoPE) -> encode V -> encode K_r (+ norms)"},
+        "roofline": roof, "stages": stages,
+        "cpu_baseline": None if args.no_cpu_baseline else step.cpu_baseline(),
+    }
+    print(json.dumps(rec))
+
+
 def cpu_baseline(step, cfg, workload):
     """Time the float64 oracle on a bounded sample of the step and scale it up."""
     import numpy as np
@@ -400,7 +523,7 @@ def cpu_baseline(step, cfg, workload):
     tokens = cfg.batch * cfg.q_len
     return {"value": tokens / secs, "unit": "query tokens/s", "cores": int(blas), "kind": "oracle",
             "sample": "; ".join(parts) + "; each stage's time scaled to the full step",
-            "seconds_per_step_extrapolated": secs}
+            "seconds_per_step": secs}
 
 
 def main():
@@ -419,6 +542,9 @@ def main():
               "shard documents across GPUs (each routes its shard, one all-gather of k candidates per "
               "sequence, a final top-k), but only the single-GPU share is built and timed.", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "encode":
+        main_encode(args)
+        return
     import torch
     import msa_inputs as mi
     dev = "cuda:0"

@@ -15,9 +15,9 @@
 // LDS, pooled rows staged in LDS and written together, non-temporal
 // accesses).  Per chunk a workgroup reads its document's offsets with scalar
 // loads: one binary search for its first chunk, then a forward walk.  The
-// rotation: a lane holds 8 (bf16) or 4 (f32) consecutive elements of one head
-// and swaps them with the lane half a head away, which holds their rotation
-// partners.  Each chunk restarts the angles exactly (position * theta in
+// rotation: a lane reads 8 bytes from each half of one head, so it holds the
+// rotation partners (x_k, x_{k+d/2}) itself and one (cos, sin) pair serves
+// two elements.  Each chunk restarts the angles exactly (position * theta in
 // float64, reduced modulo 2 pi, then sincos), and the rows inside a chunk
 // advance them by a fixed float32 rotation, so the angle error stays at a
 // few 1e-6 rad whatever the document length.
@@ -34,6 +34,11 @@ constexpr int kEncThreads = 256;
 constexpr int kEncMaxStage = 32;
 constexpr size_t kEncStageBytes = 64 * 1024;
 constexpr double kTwoPi = 6.283185307179586476925286766559;
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 load8_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
 
 // ---------------------------------------------------------------------------
 // chunk offsets: chunk_off[0] = 0, chunk_off[n+1] = chunk_off[n] + ceil(L_n / chunk)
@@ -104,20 +109,30 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
   const int red_len = (kEncThreads - seg_lanes) * N;
   char* out = reinterpret_cast<char*>(xbar);
 
-  // rotation constants of this lane's N elements (frequency f0 + e)
+  // With RoPE a lane holds N/2 elements of each half of its head (8 bytes at
+  // in_head * 8 in the low half, the same in the high half), so it holds its
+  // own rotation partners: element e < N/2 of acc is frequency f0 + e of the
+  // low half, element N/2 + e its partner.  Without RoPE a lane holds 16
+  // consecutive bytes.
+  constexpr int H2 = ROPE ? N / 2 : 1;
   const int in_head = col_lane % lanes_per_head;
-  const int half_lanes = lanes_per_head >> 1;
-  const bool low_half = in_head < half_lanes;
-  double theta[ROPE ? N : 1];
-  float cstep[ROPE ? N : 1], sstep[ROPE ? N : 1];
+  const int f0 = in_head * (N / 2);
+  double theta[H2];
+  float cstep[H2], sstep[H2];
   if constexpr (ROPE) {
-    const int f0 = (in_head % half_lanes) * N;
 #pragma unroll
-    for (int e = 0; e < N; ++e) {
+    for (int e = 0; e < H2; ++e) {
       theta[e] = exp2(-2.0 * (double)(f0 + e) / (double)dim * (double)log2_base);
       sincosf((float)fmod((double)row_groups * theta[e], kTwoPi), &sstep[e], &cstep[e]);
     }
   }
+  // byte offsets of this lane's data inside a row (lanes past the row: slot 0)
+  const size_t lo_off = !in_row ? 0
+                        : ROPE ? (size_t)(col_lane - in_head) * 16 + (size_t)in_head * 8
+                               : (size_t)col_lane * 16;
+  const size_t hi_off = lo_off + (in_row ? (size_t)lanes_per_head * 8 : 0);
+  const int st_lo = ROPE ? (lane - in_head) * 16 + in_head * 8 : lane * 16;
+  const int st_hi = st_lo + lanes_per_head * 8;
 
   if (lo >= hi) return;
   // document of the first chunk: the last n with chunk_off[n] <= lo
@@ -146,24 +161,20 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
       float acc[N];
 #pragma unroll
       for (int i = 0; i < N; ++i) acc[i] = 0.f;
-      float cs[ROPE ? N : 1], sn[ROPE ? N : 1];
+      float cs[H2], sn[H2];
       if constexpr (ROPE) {
         const double p0 = (double)(j * chunk + rg);
 #pragma unroll
-        for (int e = 0; e < N; ++e) sincosf((float)fmod(p0 * theta[e], kTwoPi), &sn[e], &cs[e]);
+        for (int e = 0; e < H2; ++e) sincosf((float)fmod(p0 * theta[e], kTwoPi), &sn[e], &cs[e]);
       }
       auto add_row = [&](const u32x4& raw) {
         float f[N];
         Vec16<T>::widen(raw, f);
         if constexpr (ROPE) {
-          u32x4 praw;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) praw[i] = (uint32_t)__shfl_xor((int)raw[i], half_lanes);
-          float g[N];
-          Vec16<T>::widen(praw, g);
-#pragma unroll
-          for (int e = 0; e < N; ++e) {
-            acc[e] += low_half ? f[e] * cs[e] - g[e] * sn[e] : f[e] * cs[e] + g[e] * sn[e];
+          for (int e = 0; e < H2; ++e) {
+            acc[e] += f[e] * cs[e] - f[H2 + e] * sn[e];
+            acc[H2 + e] += f[H2 + e] * cs[e] + f[e] * sn[e];
             const float c2 = cs[e] * cstep[e] - sn[e] * sstep[e];
             sn[e] = sn[e] * cstep[e] + cs[e] * sstep[e];
             cs[e] = c2;
@@ -173,26 +184,34 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
           for (int e = 0; e < N; ++e) acc[e] += f[e];
         }
       };
+      auto load_row = [&](const char* row) -> u32x4 {
+        if constexpr (ROPE) {
+          const u32x2 a = load8_stream(row + lo_off);
+          const u32x2 b = load8_stream(row + hi_off);
+          return u32x4{a[0], a[1], b[0], b[1]};
+        } else {
+          return load16_stream(row + lo_off);
+        }
+      };
 
-      // every lane of a row group walks the same rows (the shuffles need the
-      // whole head); lanes past the row skip the loads but not the loop
+      // every lane of a row group walks the same rows; loads are
+      // unconditional (lanes past the row read slot 0 of the same row and
+      // drop it): a branch per load would make the compiler wait for every
+      // load in flight at each join
       if (rg < row_groups) {
-        const char* base = reinterpret_cast<const char*>(x) + (size_t)r0 * row_bytes +
-                           (size_t)(in_row ? col_lane : 0) * 16;
+        const char* base = reinterpret_cast<const char*>(x) + (size_t)r0 * row_bytes;
         int r = rg;
+        const u32x4 z = {0u, 0u, 0u, 0u};
         for (; r + 7 * row_groups < cnt; r += 8 * row_groups) {
           u32x4 v[8];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            v[u] = in_row ? load16_stream(base + (size_t)(r + u * row_groups) * row_bytes) : z;
-          }
+          for (int u = 0; u < 8; ++u) v[u] = load_row(base + (size_t)(r + u * row_groups) * row_bytes);
 #pragma unroll
-          for (int u = 0; u < 8; ++u) add_row(v[u]);
+          for (int u = 0; u < 8; ++u) add_row(in_row ? v[u] : z);
         }
         for (; r < cnt; r += row_groups) {
-          const u32x4 z = {0u, 0u, 0u, 0u};
-          add_row(in_row ? load16_stream(base + (size_t)r * row_bytes) : z);
+          const u32x4 v = load_row(base + (size_t)r * row_bytes);
+          add_row(in_row ? v : z);
         }
       }
 
@@ -218,7 +237,13 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
 #pragma unroll
         for (int i = 0; i < N; ++i) mean[i] = acc[i] / div;
         const u32x4 packed = Vec16<T>::narrow(mean);
-        stage[(size_t)m * seg_lanes + lane] = packed;
+        char* srow = reinterpret_cast<char*>(stage + (size_t)m * seg_lanes);
+        if constexpr (ROPE) {
+          *reinterpret_cast<u32x2*>(srow + st_lo) = u32x2{packed[0], packed[1]};
+          *reinterpret_cast<u32x2*>(srow + st_hi) = u32x2{packed[2], packed[3]};
+        } else {
+          *reinterpret_cast<u32x4*>(srow + st_lo) = packed;
+        }
         if (norm != nullptr) {
           float stored[N];
           Vec16<T>::widen(packed, stored);
@@ -319,16 +344,12 @@ hipError_t launch_encode(const void* x, void* xbar, float* norm, const int64_t* 
                          msa_dtype dt, hipStream_t s) {
   if (total_chunks == 0 || n_docs == 0) return hipSuccess;
   const bool rope = rope_base > 0.f;
-  if (dt == MSA_F32) {
-    return rope ? launch_encode_t<float, true>(x, xbar, norm, doc_off, chunk_off, n_docs, total_rows,
-                                               total_chunks, chunk, heads, dim, rope_base, s)
-                : launch_encode_t<float, false>(x, xbar, norm, doc_off, chunk_off, n_docs, total_rows,
-                                                total_chunks, chunk, heads, dim, rope_base, s);
-  }
-  return rope ? launch_encode_t<uint16_t, true>(x, xbar, norm, doc_off, chunk_off, n_docs, total_rows,
-                                                total_chunks, chunk, heads, dim, rope_base, s)
-              : launch_encode_t<uint16_t, false>(x, xbar, norm, doc_off, chunk_off, n_docs, total_rows,
-                                                 total_chunks, chunk, heads, dim, rope_base, s);
+#define MSA_ENC(T, R)                                                                                \
+  launch_encode_t<T, R>(x, xbar, norm, doc_off, chunk_off, n_docs, total_rows, total_chunks, chunk, \
+                        heads, dim, rope_base, s)
+  if (dt == MSA_F32) return rope ? MSA_ENC(float, true) : MSA_ENC(float, false);
+  return rope ? MSA_ENC(uint16_t, true) : MSA_ENC(uint16_t, false);
+#undef MSA_ENC
 }
 
 }  // namespace msa

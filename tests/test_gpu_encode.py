@@ -68,6 +68,9 @@ def test_chunk_offsets_scan_many_documents():
     ([17, 64, 3, 90], 16, 4, 64, torch.bfloat16, 1.0e4),             # head dim 64
     ([40, 9, 100], 8, 2, 64, torch.float32, 1.0e4),                  # float32
     ([2000, 1, 2047], 64, 32, 128, torch.bfloat16, 1.0e6),          # 8 KiB rows: two column segments
+    ([300, 513, 1], 256, 8, 128, torch.bfloat16, 1.0e6),            # long chunks: many rotation steps per row group
+    ([70, 250, 3], 100, 4, 64, torch.bfloat16, 1.0e4),              # chunk not a power of two
+    ([130, 64], 64, 2, 256, torch.float32, 1.0e4),                  # float32, 1 KiB heads
 ])
 def test_encode_parity(lens, chunk, heads, dim, dtype, rope_base):
     case(f"encode lens={lens} chunk={chunk} H={heads} d={dim} {dtype} rope={rope_base}")
