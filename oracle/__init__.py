@@ -33,6 +33,8 @@ from .msa_oracle import (
     encode_docs,
     route_scores,
     topk_docs,
+    topk_docs_excluding,
+    route_rounds,
     gather_kv,
     sparse_attention,
     sparse_attention_rows,
@@ -51,6 +53,8 @@ __all__ = [
     "encode_docs",
     "route_scores",
     "topk_docs",
+    "topk_docs_excluding",
+    "route_rounds",
     "gather_kv",
     "sparse_attention",
     "sparse_attention_rows",

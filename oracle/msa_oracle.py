@@ -236,6 +236,66 @@ def topk_docs(scores, k):
 
 
 # ---------------------------------------------------------------------------
+# Memory Interleave: several routing rounds, each excluding earlier picks
+# ---------------------------------------------------------------------------
+
+def topk_docs_excluding(scores, k, exclude):
+    """The k best documents per sequence among those not in its exclusion set.
+
+    ``exclude[b]`` lists the ids sequence b may not select (a list per
+    sequence, or a [B, n] integer array); ids outside [0, N_doc) are ignored,
+    so -1 may pad a row, and repeated ids count once.  The order and the tie
+    rule are those of :func:`topk_docs`.  Raises ValueError when fewer than k
+    documents remain.  Returns (ids int64 [B, k], values float64 [B, k]).
+
+    Reading ([README] "Inference Pipeline", Figure 3, and the page's FAQ on
+    Memory Interleave: routing may run for several rounds, each round jumping
+    to further memory segments): a later round does not pick a document an
+    earlier round already brought into the context.
+    """
+    s = np.asarray(scores, dtype=np.float64)
+    b_, n = s.shape
+    if not 1 <= k <= n:
+        raise ValueError("k must lie in [1, N_doc]")
+    ids = np.empty((b_, k), dtype=np.int64)
+    vals = np.empty((b_, k), dtype=np.float64)
+    for b in range(b_):
+        banned = {int(i) for i in np.asarray(exclude[b]).reshape(-1) if 0 <= int(i) < n}
+        allowed = np.array([d for d in range(n) if d not in banned], dtype=np.int64)
+        if allowed.size < k:
+            raise ValueError("fewer than k documents remain after the exclusion")
+        order = np.lexsort((allowed, -s[b, allowed]))
+        ids[b] = allowed[order[:k]]
+        vals[b] = s[b, ids[b]]
+    return ids, vals
+
+
+def route_rounds(q_r_rounds, kbar_r, chunks_per_doc, k, eps=EPS):
+    """Multi-round routing (Memory Interleave), kernel level.
+
+    Round r routes its own router query ``q_r_rounds[r]`` ([B, T, H, d]; the
+    model produces it between rounds) against the bank as in
+    :func:`route_scores`, then takes the top-k among the documents no earlier
+    round selected (:func:`topk_docs_excluding`).  Returns (ids int64 [B, R*k],
+    values float64 [B, R*k]): round r's picks in columns [r*k, (r+1)*k), each
+    round in rank order.  Reading: the rounds' documents are concatenated in
+    round order, and the gathered memory follows that order.
+    """
+    q = [np.asarray(x, dtype=np.float64) for x in q_r_rounds]
+    if not q:
+        raise ValueError("at least one round")
+    b_ = q[0].shape[0]
+    ids = np.empty((b_, 0), dtype=np.int64)
+    vals = np.empty((b_, 0), dtype=np.float64)
+    for qr in q:
+        s = route_scores(qr, kbar_r, chunks_per_doc, eps=eps)
+        i_r, v_r = topk_docs_excluding(s, k, ids)
+        ids = np.concatenate([ids, i_r], axis=1)
+        vals = np.concatenate([vals, v_r], axis=1)
+    return ids, vals
+
+
+# ---------------------------------------------------------------------------
 # S4: gather of the selected documents' pooled K/V
 # ---------------------------------------------------------------------------
 
