@@ -162,6 +162,52 @@ msa_status msa_topk_docs(const float* doc_scores, int32_t batch, int64_t n_docs,
                          void* stream);
 
 /* ------------------------------------------------------------------------
+ * Multi-round routing, "Memory Interleave" (MSA README "Inference Pipeline",
+ *     Figure 3: an optional multi-round interleave for multi-hop questions;
+ *     the same page's FAQ: the rounds jump across scattered memory segments).
+ *     Kernel level only: how the model forms each round's router query is
+ *     not part of this library.  Reading: a round never re-selects a document
+ *     an earlier round selected, and the rounds' picks are concatenated in
+ *     round order.
+ *
+ * msa_topk_docs_excluding: msa_topk_docs over the documents of row b that are
+ *   not among excl_ids[b*excl_stride + 0 .. n_excl-1] (int32, device).
+ *   Excluded ids outside [0, n_docs) are ignored (-1 may pad a row); repeated
+ *   ids count once.  Row b's results go to topk_ids[b*out_stride + 0 .. k-1]
+ *   (and topk_scores likewise, or NULL).  Requires k + n_excl <= n_docs (k
+ *   documents always remain), excl_stride >= n_excl, out_stride >= k; the
+ *   workspace is msa_topk_docs_workspace(batch, n_docs, k).  The exclusion
+ *   entries may share the output buffer only in the multi-round layout (equal
+ *   strides, row b's outputs after its n_excl entries, e.g. excl_ids = ids,
+ *   topk_ids = ids + n_excl); other overlaps return MSA_ERR_INVALID.
+ *
+ * msa_route_rounds: `rounds` rounds on `stream`; round r routes
+ *   q_r[r] as msa_route_scores does, then keeps the top-k of the documents no
+ *   earlier round selected (msa_topk_docs_excluding).
+ *   q_r          [rounds, batch, q_len, heads, dim]  (dtype dt)
+ *   kbar_r, kbar_r_norm as for msa_route_scores
+ *   topk_ids     [batch, rounds*k] int32 output: round r in columns [r*k, (r+1)*k)
+ *   topk_scores  [batch, rounds*k] float32 output, or NULL
+ *   ws           msa_route_rounds_workspace() bytes (the per-round scores
+ *                plus the route / top-k scratch); 16-byte aligned
+ *   Requires 1 <= rounds, rounds*k <= n_docs, k <= 1024.  The batch*rounds*k
+ *   ids are distinct per row; msa_gather_kv with k' = rounds*k then gives the
+ *   memory rows in round order.
+ * ---------------------------------------------------------------------- */
+msa_status msa_topk_docs_excluding(const float* doc_scores, int32_t batch, int64_t n_docs, int32_t k,
+                                   const int32_t* excl_ids, int32_t n_excl, int64_t excl_stride,
+                                   int32_t* topk_ids, float* topk_scores, int64_t out_stride, void* ws,
+                                   size_t ws_bytes, void* stream);
+msa_status msa_route_rounds_workspace(int32_t rounds, int32_t batch, int32_t q_len, int32_t heads,
+                                      int32_t dim, int64_t n_docs, int32_t chunks_per_doc, int32_t k,
+                                      msa_dtype dt, size_t* bytes);
+msa_status msa_route_rounds(const void* q_r, const void* kbar_r, const float* kbar_r_norm,
+                            int32_t rounds, int32_t batch, int32_t q_len, int32_t heads, int32_t dim,
+                            int64_t n_docs, int32_t chunks_per_doc, int32_t k, msa_dtype dt,
+                            int32_t* topk_ids, float* topk_scores, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* ------------------------------------------------------------------------
  * S4  Gather of the selected documents' pooled K/V ("Inference Pipeline",
  *     stage 2: load only the selected pooled K/V; the content tier may live
  *     in host DRAM and be fetched when selected).

@@ -3,13 +3,15 @@
 The work runs in hand-written HIP kernels in ``libmsa.so`` behind the C ABI
 of ``include/msa.h``; this package is its thin Python binding:
 
-    msa_pool_chunks    S1  chunk-mean pooling of K / V / K_r into the bank
-    msa_chunk_offsets  \   offline encoder over variable-length documents:
-    msa_encode_docs    /   document-wise RoPE + chunk means (+ norms)
-    msa_route_scores   S2  cosine routing scores per document
-    msa_topk_docs      S3  top-k documents
-    msa_gather_kv      S4  gather (or host-tier fetch) of the selected pooled K/V
-    msa_sparse_attn    S5/S6 sparse GQA attention (prefill and decode)
+    msa_pool_chunks          S1  chunk-mean pooling of K / V / K_r into the bank
+    msa_chunk_offsets        offline encoder over variable-length documents:
+    msa_encode_docs            document-wise RoPE + chunk means (+ norms)
+    msa_route_scores         S2  cosine routing scores per document
+    msa_topk_docs            S3  top-k documents
+    msa_topk_docs_excluding  top-k among the documents not yet selected
+    msa_route_rounds         multi-round routing (Memory Interleave)
+    msa_gather_kv            S4  gather (or host-tier fetch) of the selected pooled K/V
+    msa_sparse_attn          S5/S6 sparse GQA attention (prefill and decode)
 """
 
 from ._lib import (  # noqa: F401
@@ -20,11 +22,14 @@ from ._lib import (  # noqa: F401
     msa_encode_docs,
     msa_gather_kv,
     msa_pool_chunks,
+    msa_route_rounds,
+    msa_route_rounds_workspace,
     msa_route_scores,
     msa_route_scores_workspace,
     msa_sparse_attn,
     msa_sparse_attn_workspace,
     msa_topk_docs,
+    msa_topk_docs_excluding,
     msa_topk_docs_workspace,
     SIGNATURES,
 )

@@ -38,6 +38,13 @@ SIGNATURES = {
     "msa_topk_docs_workspace": (_STATUS, [c_int32, c_int64, c_int32, POINTER(c_size_t)]),
     "msa_topk_docs": (_STATUS, [c_void_p, c_int32, c_int64, c_int32, c_void_p, c_void_p, c_void_p,
                                 c_size_t, c_void_p]),
+    "msa_topk_docs_excluding": (_STATUS, [c_void_p, c_int32, c_int64, c_int32, c_void_p, c_int32, c_int64,
+                                          c_void_p, c_void_p, c_int64, c_void_p, c_size_t, c_void_p]),
+    "msa_route_rounds_workspace": (_STATUS, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int64, c_int32,
+                                             c_int32, c_int, POINTER(c_size_t)]),
+    "msa_route_rounds": (_STATUS, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                   c_int64, c_int32, c_int32, c_int, c_void_p, c_void_p, c_void_p, c_size_t,
+                                   c_void_p]),
     "msa_gather_kv": (_STATUS, [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int64,
                                 c_int32, c_int32, c_int32, c_int, c_void_p, c_void_p, c_int32,
                                 c_void_p]),
@@ -253,6 +260,81 @@ def msa_topk_docs(doc_scores, k, topk_ids=None, topk_scores=None, with_scores=Tr
     ws, ws_bytes = _workspace(msa_topk_docs_workspace(batch, n_docs, k), doc_scores.device, ws)
     _check(lib().msa_topk_docs(_ptr(doc_scores), batch, n_docs, k, _ptr(topk_ids), _ptr(topk_scores),
                                _ptr(ws), ws_bytes, _stream(doc_scores.device)))
+    return topk_ids, topk_scores
+
+
+# ---------------------------------------------------------------------------
+# Multi-round routing (Memory Interleave)
+# ---------------------------------------------------------------------------
+
+def msa_topk_docs_excluding(doc_scores, k, excl_ids, topk_ids=None, topk_scores=None, with_scores=True,
+                            ws=None):
+    """Top-k document ids [batch, k] int32 (and scores) of ``doc_scores`` [batch, n_docs] among the
+    documents not listed in ``excl_ids`` [batch, n_excl] int32 (ids outside [0, n_docs) ignored)."""
+    _dev(doc_scores, "doc_scores", dtype=torch.float32, ndim=2)
+    _dev(excl_ids, "excl_ids", dtype=torch.int32, ndim=2)
+    batch, n_docs = doc_scores.shape
+    if excl_ids.shape[0] != batch:
+        raise ValueError("excl_ids must have one row per sequence")
+    n_excl = excl_ids.shape[1]
+    if topk_ids is None:
+        topk_ids = torch.empty((batch, k), dtype=torch.int32, device=doc_scores.device)
+    _dev(topk_ids, "topk_ids", dtype=torch.int32)
+    if topk_ids.shape != (batch, k):
+        raise ValueError("topk_ids must be [batch, k]")
+    if with_scores and topk_scores is None:
+        topk_scores = torch.empty((batch, k), dtype=torch.float32, device=doc_scores.device)
+    if topk_scores is not None:
+        _dev(topk_scores, "topk_scores", dtype=torch.float32)
+        if topk_scores.shape != (batch, k):
+            raise ValueError("topk_scores must be [batch, k]")
+    ws, ws_bytes = _workspace(msa_topk_docs_workspace(batch, n_docs, k), doc_scores.device, ws)
+    _check(lib().msa_topk_docs_excluding(_ptr(doc_scores), batch, n_docs, k, _ptr(excl_ids), n_excl, n_excl,
+                                         _ptr(topk_ids), _ptr(topk_scores), k, _ptr(ws), ws_bytes,
+                                         _stream(doc_scores.device)))
+    return topk_ids, topk_scores
+
+
+def msa_route_rounds_workspace(rounds, batch, q_len, heads, dim, n_docs, chunks_per_doc, k, dtype):
+    n = c_size_t(0)
+    code = MSA_F32 if dtype == torch.float32 else MSA_BF16
+    _check(lib().msa_route_rounds_workspace(rounds, batch, q_len, heads, dim, n_docs, chunks_per_doc, k, code,
+                                            ctypes.byref(n)))
+    return n.value
+
+
+def msa_route_rounds(q_r, kbar_r, kbar_r_norm, chunks_per_doc, k, topk_ids=None, topk_scores=None,
+                     with_scores=True, ws=None):
+    """Multi-round routing: ``q_r`` [rounds, batch, q_len, heads, dim] holds one router query per
+    round; round r routes its query and keeps the top-k documents no earlier round selected.
+    Returns ids [batch, rounds*k] int32 (round r in columns [r*k, (r+1)*k)) and their scores."""
+    _dev(q_r, "q_r", ndim=5)
+    _dev(kbar_r, "kbar_r", dtype=q_r.dtype, ndim=3)
+    _dev(kbar_r_norm, "kbar_r_norm", dtype=torch.float32, ndim=2)
+    rounds, batch, q_len, heads, dim = q_r.shape
+    n_ch = kbar_r.shape[0]
+    if kbar_r.shape[1:] != (heads, dim) or kbar_r_norm.shape != (n_ch, heads):
+        raise ValueError("router queries, pooled keys and norms disagree in shape")
+    if n_ch % chunks_per_doc:
+        raise ValueError("chunk count is not a multiple of chunks_per_doc")
+    n_docs = n_ch // chunks_per_doc
+    dev = q_r.device
+    if topk_ids is None:
+        topk_ids = torch.empty((batch, rounds * k), dtype=torch.int32, device=dev)
+    _dev(topk_ids, "topk_ids", dtype=torch.int32)
+    if topk_ids.shape != (batch, rounds * k):
+        raise ValueError("topk_ids must be [batch, rounds*k]")
+    if with_scores and topk_scores is None:
+        topk_scores = torch.empty((batch, rounds * k), dtype=torch.float32, device=dev)
+    if topk_scores is not None:
+        _dev(topk_scores, "topk_scores", dtype=torch.float32)
+        if topk_scores.shape != (batch, rounds * k):
+            raise ValueError("topk_scores must be [batch, rounds*k]")
+    nbytes = msa_route_rounds_workspace(rounds, batch, q_len, heads, dim, n_docs, chunks_per_doc, k, q_r.dtype)
+    ws, ws_bytes = _workspace(nbytes, dev, ws)
+    _check(lib().msa_route_rounds(_ptr(q_r), _ptr(kbar_r), _ptr(kbar_r_norm), rounds, batch, q_len, heads, dim,
+                                  n_docs, chunks_per_doc, k, _dtype_code(q_r), _ptr(topk_ids), _ptr(topk_scores),
+                                  _ptr(ws), ws_bytes, _stream(dev)))
     return topk_ids, topk_scores
 
 

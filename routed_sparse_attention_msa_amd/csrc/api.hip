@@ -3,6 +3,7 @@
 // in the HIP kernels behind the launch_* functions.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <mutex>
@@ -231,6 +232,108 @@ msa_status msa_topk_docs(const float* doc_scores, int32_t batch, int64_t n_docs,
   return hip_status(msa::launch_topk(doc_scores, batch, n_docs, k, topk_ids, topk_scores, ws,
                                      static_cast<hipStream_t>(stream)),
                     "msa_topk_docs launch");
+}
+
+// ---------------------------------------------------------------------------
+// Multi-round routing (Memory Interleave)
+
+// Exclusion entries may share the output buffer only in the multi-round
+// layout: equal row strides, each row's k outputs after its own n_excl
+// exclusion entries and before the next row.
+static bool excl_layout_ok(const int32_t* excl, int64_t es, int n_excl, const int32_t* out, int64_t os,
+                           int k, int batch) {
+  if (excl == nullptr || n_excl == 0) return true;
+  const int32_t* e_end = excl + (size_t)(batch - 1) * (size_t)es + n_excl;
+  const int32_t* o_end = out + (size_t)(batch - 1) * (size_t)os + k;
+  if (e_end <= out || o_end <= excl) return true;
+  if (es != os) return false;
+  const ptrdiff_t d = out - excl;
+  return d >= n_excl && d + k <= es;
+}
+
+msa_status msa_topk_docs_excluding(const float* doc_scores, int32_t batch, int64_t n_docs, int32_t k,
+                                   const int32_t* excl_ids, int32_t n_excl, int64_t excl_stride,
+                                   int32_t* topk_ids, float* topk_scores, int64_t out_stride, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  msa_status st = check_topk(batch, n_docs, k);
+  if (st != MSA_OK) return st;
+  CHECK_ARG(n_excl >= 0 && (int64_t)k + n_excl <= n_docs,
+            "need n_excl >= 0 and k + n_excl <= n_docs (k=%d n_excl=%d n_docs=%lld)", k, n_excl,
+            (long long)n_docs);
+  CHECK_ARG(n_excl == 0 || (excl_ids != nullptr && excl_stride >= n_excl),
+            "excl_ids missing or excl_stride < n_excl");
+  CHECK_ARG(out_stride >= k, "out_stride < k");
+  CHECK_ARG(doc_scores && topk_ids, "null tensor pointer");
+  CHECK_ARG(((uintptr_t)topk_ids & 3u) == 0 && ((uintptr_t)excl_ids & 3u) == 0, "id arrays misaligned");
+  CHECK_ARG(excl_layout_ok(excl_ids, excl_stride, n_excl, topk_ids, out_stride, k, batch),
+            "exclusion entries overlap the outputs");
+  const size_t need = msa::topk_workspace_bytes(batch, n_docs, k);
+  CHECK_ARG(ws_bytes >= need, "workspace too small (%zu < %zu bytes)", ws_bytes, need);
+  CHECK_ARG(need == 0 || (ws != nullptr && aligned16(ws)), "workspace pointer missing or misaligned");
+  return hip_status(msa::launch_topk_excl(doc_scores, batch, n_docs, k, excl_ids, n_excl, excl_stride,
+                                          topk_ids, topk_scores, out_stride, ws,
+                                          static_cast<hipStream_t>(stream)),
+                    "msa_topk_docs_excluding launch");
+}
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+static msa_status rounds_workspace(int32_t rounds, int32_t batch, int32_t q_len, int32_t heads,
+                                   int32_t dim, int64_t n_docs, int32_t cpd, int32_t k, msa_dtype dt,
+                                   size_t* scores_bytes, size_t* total) {
+  msa_status st = check_route(batch, q_len, heads, dim, n_docs, cpd, dt);
+  if (st != MSA_OK) return st;
+  if ((st = check_topk(batch, n_docs, k)) != MSA_OK) return st;
+  CHECK_ARG(rounds >= 1 && (int64_t)rounds * k <= n_docs,
+            "need rounds >= 1 and rounds*k <= n_docs (rounds=%d k=%d n_docs=%lld)", rounds, k,
+            (long long)n_docs);
+  *scores_bytes = align256((size_t)batch * (size_t)n_docs * sizeof(float));
+  *total = *scores_bytes + std::max(msa::route_workspace_bytes(batch, q_len, heads, dim, n_docs, cpd, dt),
+                                    msa::topk_workspace_bytes(batch, n_docs, k));
+  return MSA_OK;
+}
+
+msa_status msa_route_rounds_workspace(int32_t rounds, int32_t batch, int32_t q_len, int32_t heads,
+                                      int32_t dim, int64_t n_docs, int32_t chunks_per_doc, int32_t k,
+                                      msa_dtype dt, size_t* bytes) {
+  size_t sb = 0, total = 0;
+  msa_status st = rounds_workspace(rounds, batch, q_len, heads, dim, n_docs, chunks_per_doc, k, dt, &sb,
+                                   &total);
+  if (st != MSA_OK) return st;
+  CHECK_ARG(bytes != nullptr, "bytes is null");
+  *bytes = total;
+  return MSA_OK;
+}
+
+msa_status msa_route_rounds(const void* q_r, const void* kbar_r, const float* kbar_r_norm,
+                            int32_t rounds, int32_t batch, int32_t q_len, int32_t heads, int32_t dim,
+                            int64_t n_docs, int32_t chunks_per_doc, int32_t k, msa_dtype dt,
+                            int32_t* topk_ids, float* topk_scores, void* ws, size_t ws_bytes,
+                            void* stream) {
+  size_t sb = 0, total = 0;
+  msa_status st = rounds_workspace(rounds, batch, q_len, heads, dim, n_docs, chunks_per_doc, k, dt, &sb,
+                                   &total);
+  if (st != MSA_OK) return st;
+  CHECK_ARG(q_r && kbar_r && kbar_r_norm && topk_ids, "null tensor pointer");
+  CHECK_ARG(aligned16(q_r) && aligned16(kbar_r) && aligned16(kbar_r_norm), "tensors must be 16-byte aligned");
+  CHECK_ARG(((uintptr_t)topk_ids & 3u) == 0 && ((uintptr_t)topk_scores & 3u) == 0, "outputs misaligned");
+  CHECK_ARG(ws_bytes >= total, "workspace too small (%zu < %zu bytes)", ws_bytes, total);
+  CHECK_ARG(ws != nullptr && aligned16(ws), "workspace pointer missing or misaligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* scores = static_cast<float*>(ws);
+  void* scratch = static_cast<char*>(ws) + sb;
+  const size_t q_bytes = (size_t)batch * q_len * heads * dim * dtype_size(dt);
+  const int64_t stride = (int64_t)rounds * k;
+  for (int r = 0; r < rounds; ++r) {
+    const void* q = static_cast<const char*>(q_r) + (size_t)r * q_bytes;
+    hipError_t e = msa::launch_route(q, kbar_r, kbar_r_norm, batch, q_len, heads, dim, n_docs,
+                                     chunks_per_doc, dt, scores, scratch, s);
+    if (e != hipSuccess) return hip_status(e, "msa_route_rounds route launch");
+    e = msa::launch_topk_excl(scores, batch, n_docs, k, topk_ids, r * k, stride, topk_ids + (size_t)r * k,
+                              topk_scores ? topk_scores + (size_t)r * k : nullptr, stride, scratch, s);
+    if (e != hipSuccess) return hip_status(e, "msa_route_rounds top-k launch");
+  }
+  return MSA_OK;
 }
 
 // ---------------------------------------------------------------------------

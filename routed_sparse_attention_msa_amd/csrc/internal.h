@@ -115,6 +115,11 @@ hipError_t launch_route(const void* q_r, const void* kbar_r, const float* knorm,
 size_t topk_workspace_bytes(int batch, int64_t n_docs, int k);
 hipError_t launch_topk(const float* scores, int batch, int64_t n_docs, int k, int32_t* ids,
                        float* vals, void* ws, hipStream_t s);
+// As launch_topk over the documents not in excl[b*excl_stride + 0..n_excl-1]
+// (ids outside [0, n_docs) ignored); outputs at row b*out_stride.
+hipError_t launch_topk_excl(const float* scores, int batch, int64_t n_docs, int k, const int32_t* excl,
+                            int n_excl, int64_t excl_stride, int32_t* ids, float* vals,
+                            int64_t out_stride, void* ws, hipStream_t s);
 
 hipError_t launch_gather(const void* kbar, const void* vbar, const int32_t* ids, int batch, int k,
                          int64_t n_docs, int cpd, size_t row_bytes, void* k_sel, void* v_sel,

@@ -16,6 +16,12 @@
 // The k winners are appended to LDS and ordered with a bitonic network.
 // Rows longer than one tile are reduced in rounds: every tile emits its k
 // best keys to the workspace, and the next round selects among those.
+//
+// Exclusion (multi-round routing, MSA README "Inference Pipeline", Figure 3,
+// and the page's FAQ on Memory Interleave: a later routing round skips the
+// documents earlier rounds selected): each first-round tile marks the
+// excluded ids that fall in its 4096-id range in an LDS bitmap and drops
+// those keys before the select.
 #include "internal.h"
 
 namespace msa {
@@ -43,6 +49,7 @@ __device__ __forceinline__ uint64_t make_key(float s, uint32_t id) {
 
 struct Smem {
   uint64_t list[kMaxK];
+  uint32_t excl_bits[kTile / 32];
   uint32_t hist[256];
   uint32_t wave_sum[kThreads / 64];
   uint32_t count;
@@ -147,20 +154,34 @@ __device__ void block_select(const uint64_t (&key)[kItems], const bool (&valid)[
 // One tile of one row.  FROM_KEYS: the input is a previous round's keys
 // (0 = padding); otherwise raw float scores whose ids are their positions.
 // FINAL: write ids/scores; otherwise write the tile's k best keys.
+// Exclusion (raw-score rounds only): excl[b * excl_stride + j], j < n_excl;
+// ids outside [0, n) are ignored.  Outputs of FINAL go to row b * out_stride.
 template <bool FROM_KEYS, bool FINAL>
 __global__ __launch_bounds__(kThreads) void topk_tile_kernel(
     const float* __restrict__ scores, const uint64_t* __restrict__ keys_in, int64_t n, int k,
-    int kp2, uint64_t* __restrict__ keys_out, int32_t* __restrict__ ids_out,
-    float* __restrict__ vals_out) {
+    int kp2, const int32_t* excl, int n_excl, int64_t excl_stride, uint64_t* __restrict__ keys_out,
+    int32_t* ids_out, float* vals_out, int64_t out_stride) {
   __shared__ Smem sm;
   const int b = blockIdx.y;
   const int64_t base = (int64_t)blockIdx.x * kTile;
+  const bool any_excl = !FROM_KEYS && n_excl > 0;
+  if (any_excl) {
+    for (int i = threadIdx.x; i < kTile / 32; i += kThreads) sm.excl_bits[i] = 0;
+    __syncthreads();
+    for (int j = threadIdx.x; j < n_excl; j += kThreads) {
+      const int64_t id = excl[(size_t)b * excl_stride + j];
+      const int64_t rel = id - base;
+      if (id >= 0 && id < n && rel >= 0 && rel < kTile) atomicOr(&sm.excl_bits[rel >> 5], 1u << (rel & 31));
+    }
+    __syncthreads();
+  }
   uint64_t key[kItems];
   bool valid[kItems];
 #pragma unroll
   for (int i = 0; i < kItems; ++i) {
-    const int64_t idx = base + i * kThreads + threadIdx.x;
-    valid[i] = idx < n;
+    const int rel = i * kThreads + threadIdx.x;
+    const int64_t idx = base + rel;
+    valid[i] = idx < n && !(any_excl && ((sm.excl_bits[rel >> 5] >> (rel & 31)) & 1u));
     key[i] = 0;
     if (valid[i]) {
       if (FROM_KEYS) {
@@ -175,8 +196,8 @@ __global__ __launch_bounds__(kThreads) void topk_tile_kernel(
   for (int i = threadIdx.x; i < k; i += kThreads) {
     const uint64_t kk = sm.list[i];
     if (FINAL) {
-      ids_out[(size_t)b * k + i] = (int32_t)(0xFFFFFFFFu - (uint32_t)kk);
-      if (vals_out) vals_out[(size_t)b * k + i] = unorder_score((uint32_t)(kk >> 32));
+      ids_out[(size_t)b * out_stride + i] = (int32_t)(0xFFFFFFFFu - (uint32_t)kk);
+      if (vals_out) vals_out[(size_t)b * out_stride + i] = unorder_score((uint32_t)(kk >> 32));
     } else {
       keys_out[((size_t)b * gridDim.x + blockIdx.x) * k + i] = kk;
     }
@@ -199,30 +220,38 @@ size_t topk_workspace_bytes(int batch, int64_t n_docs, int k) {
 
 hipError_t launch_topk(const float* scores, int batch, int64_t n_docs, int k, int32_t* ids,
                        float* vals, void* ws, hipStream_t s) {
+  return launch_topk_excl(scores, batch, n_docs, k, nullptr, 0, 0, ids, vals, k, ws, s);
+}
+
+hipError_t launch_topk_excl(const float* scores, int batch, int64_t n_docs, int k, const int32_t* excl,
+                            int n_excl, int64_t excl_stride, int32_t* ids, float* vals,
+                            int64_t out_stride, void* ws, hipStream_t s) {
   const int kp2 = next_pow2(k);
   int64_t tiles = (n_docs + kTile - 1) / kTile;
   if (tiles <= 1) {
     hipLaunchKernelGGL((topk_tile_kernel<false, true>), dim3(1, batch), dim3(kThreads), 0, s,
-                       scores, nullptr, n_docs, k, kp2, nullptr, ids, vals);
+                       scores, nullptr, n_docs, k, kp2, excl, n_excl, excl_stride, nullptr, ids, vals,
+                       out_stride);
     return hipGetLastError();
   }
   uint64_t* buf[2];
   buf[0] = static_cast<uint64_t*>(ws);
   buf[1] = buf[0] + (size_t)batch * (size_t)tiles * (size_t)k;
   hipLaunchKernelGGL((topk_tile_kernel<false, false>), dim3((unsigned)tiles, batch), dim3(kThreads),
-                     0, s, scores, nullptr, n_docs, k, kp2, buf[0], nullptr, nullptr);
+                     0, s, scores, nullptr, n_docs, k, kp2, excl, n_excl, excl_stride, buf[0], nullptr,
+                     nullptr, 0);
   int cur = 0;
   int64_t n = tiles * k;
   for (;;) {
     tiles = (n + kTile - 1) / kTile;
     if (tiles == 1) {
       hipLaunchKernelGGL((topk_tile_kernel<true, true>), dim3(1, batch), dim3(kThreads), 0, s,
-                         nullptr, buf[cur], n, k, kp2, nullptr, ids, vals);
+                         nullptr, buf[cur], n, k, kp2, nullptr, 0, 0, nullptr, ids, vals, out_stride);
       break;
     }
     hipLaunchKernelGGL((topk_tile_kernel<true, false>), dim3((unsigned)tiles, batch),
-                       dim3(kThreads), 0, s, nullptr, buf[cur], n, k, kp2, buf[cur ^ 1], nullptr,
-                       nullptr);
+                       dim3(kThreads), 0, s, nullptr, buf[cur], n, k, kp2, nullptr, 0, 0, buf[cur ^ 1],
+                       nullptr, nullptr, 0);
     cur ^= 1;
     n = tiles * k;
   }

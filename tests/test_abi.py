@@ -96,6 +96,33 @@ def test_topk_validation_and_workspace():
     assert "workspace" in _err()
 
 
+def test_rounds_validation():
+    lib = msa.lib()
+    p = ctypes.c_void_p(256)
+    n = ctypes.c_size_t(0)
+    # k + n_excl must leave k documents; strides must hold the rows
+    assert lib.msa_topk_docs_excluding(p, 2, 100, 10, p, 91, 91, p, None, 10, None, 0, None) == L.MSA_ERR_INVALID
+    assert "k + n_excl" in _err()
+    assert lib.msa_topk_docs_excluding(p, 2, 100, 10, p, 5, 4, p, None, 10, None, 0, None) == L.MSA_ERR_INVALID
+    assert lib.msa_topk_docs_excluding(p, 2, 100, 10, None, 5, 5, p, None, 10, None, 0, None) == L.MSA_ERR_INVALID
+    assert lib.msa_topk_docs_excluding(p, 2, 100, 10, None, 0, 0, p, None, 9, None, 0, None) == L.MSA_ERR_INVALID
+    # exclusion entries inside the outputs: only the multi-round layout is accepted
+    ids = 4096
+    ok = (ctypes.c_void_p(ids), ctypes.c_void_p(ids + 4 * 8))          # excl = ids, out = ids + 8 (n_excl 8)
+    bad = (ctypes.c_void_p(ids), ctypes.c_void_p(ids + 4 * 4))         # out starts inside the exclusion
+    assert lib.msa_topk_docs_excluding(p, 2, 100, 4, ok[0], 8, 12, bad[1], None, 12, None, 0, None) == L.MSA_ERR_INVALID
+    assert "overlap" in _err()
+    assert lib.msa_topk_docs_excluding(p, 2, 100, 4, ok[0], 8, 12, ok[1], None, 16, None, 0, None) == L.MSA_ERR_INVALID
+    # rounds * k may not exceed the documents
+    assert lib.msa_route_rounds_workspace(3, 1, 8, 8, 128, 40, 8, 16, L.MSA_BF16, ctypes.byref(n)) == L.MSA_ERR_INVALID
+    assert lib.msa_route_rounds_workspace(0, 1, 8, 8, 128, 40, 8, 4, L.MSA_BF16, ctypes.byref(n)) == L.MSA_ERR_INVALID
+    assert lib.msa_route_rounds_workspace(3, 2, 8, 8, 128, 48, 8, 16, L.MSA_BF16, ctypes.byref(n)) == L.MSA_OK
+    assert n.value >= 2 * 48 * 4
+    assert lib.msa_route_rounds(p, p, p, 3, 2, 8, 8, 128, 48, 8, 16, L.MSA_BF16, p, None, None, 0,
+                                None) == L.MSA_ERR_INVALID
+    assert "workspace" in _err()
+
+
 def test_route_validation():
     lib = msa.lib()
     p = ctypes.c_void_p(256)
