@@ -1,6 +1,7 @@
 """Benchmark of the MSA routed-layer hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode|encode] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode|interleave|encode]
+                    [--no-cpu-baseline]
 
 A step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM:
@@ -11,6 +12,11 @@ already resident in HBM:
   decode  (the same bank; 32 sequences x 1 token, 4096 cached tokens, top-16):
       route -> top-k -> gather -> split-KV attention (the bank is pooled once,
       outside the timed region, as the offline stage of the pipeline)
+  interleave (the prefill workload with 3 routing rounds, Memory Interleave at
+           kernel level: each round routes its own planted router query and
+           keeps the top-16 documents no earlier round took; the 48 documents'
+           memory, 384 pooled rows, then joins the prefill attention):
+      route+top-k x3 -> gather -> attention (the bank is pooled outside the step)
   encode  (offline encoder: 2048 documents of 256..768 tokens, ~1M tokens,
            8 KV heads x 128, bf16): chunk offsets -> encode K (document-wise
            RoPE, base 1e6) -> encode V -> encode K_r (+ norms)
@@ -36,6 +42,7 @@ file is unchanged (sha256 recorded beside it).
 """
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -55,7 +62,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", choices=["prefill", "decode", "encode"], default="prefill")
+    p.add_argument("--workload", choices=["prefill", "decode", "interleave", "encode"], default="prefill")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     # profiling helpers (see "Profiles" in the module docstring)
@@ -87,6 +94,13 @@ def work_route(cfg):
     b = cfg.n_chunks * row * 2 + cfg.n_chunks * cfg.heads_kv * 4 + t_tot * row * 2 + cfg.batch * cfg.n_doc * 4
     ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     return {"bound": "mfma" if flops / b > ridge else "hbm", "bytes": b, "flops": flops}
+
+
+def work_rounds(cfg, rounds):
+    # the routing of every round (MFMA-bound at 2048 tokens); the top-k launches are latency
+    w = work_route(cfg)
+    return {"bound": w["bound"], "bytes": rounds * (w["bytes"] + work_topk(cfg)["bytes"]),
+            "flops": rounds * w["flops"]}
 
 
 def work_topk(cfg):
@@ -138,10 +152,13 @@ STAGE_KERNELS = {
                 "attn": ("attn_prefill", "attn_prefill.hip")},
     "decode": {"route": ("route_", "route.hip"), "topk": ("topk", "topk.hip"),
                "gather": ("gather", "gather.hip"), "attn": ("attn_decode", "attn_decode.hip")},
+    "interleave": {"rounds": ("route_", "route.hip"), "gather": ("gather", "gather.hip"),
+                   "attn": ("attn_prefill", "attn_prefill.hip")},
     "encode": {"offsets": ("chunk_offsets", "encode.hip"), "encode": ("encode_kernel", "encode.hip")},
     # (both encode launches share one kernel template; the traffic entry covers their average)
 }
 COPY_PROBE_BYTES = 1 << 30
+INTERLEAVE_ROUNDS = 3
 
 
 def measured_traffic(workload, stage):
@@ -268,12 +285,12 @@ def copy_probe():
 class Step:
     """Preallocated buffers and the sequence of ABI calls of one step."""
 
-    def __init__(self, cfg, workload, seed, dev):
+    def __init__(self, cfg, workload, seed, dev, rounds=1):
         import torch
         import msa_inputs as mi
         import routed_sparse_attention_msa_amd as msa
-        self.torch, self.msa, self.cfg, self.workload = torch, msa, cfg, workload
-        t = mi.draw_layer(cfg if workload == "prefill" else mi.PREFILL, seed=seed, device=dev)
+        self.torch, self.msa, self.cfg, self.workload, self.rounds = torch, msa, cfg, workload, rounds
+        t = mi.draw_layer(cfg if workload != "decode" else mi.PREFILL, seed=seed, device=dev)
         if workload == "decode":
             d = mi.draw_layer(cfg, seed=seed + 1, device=dev, with_raw=False)
             for k in ("q", "k_loc", "v_loc", "q_r"):
@@ -288,11 +305,19 @@ class Step:
         self._pool()
         if "q_r" not in t:
             t["q_r"] = mi.plant_router_queries(self.kbar_r, t["planted"], t["q_r_noise"], cfg)
+        if workload == "interleave":
+            # round r > 0: its own planted documents and noise (a later seed)
+            qs = [t["q_r"]]
+            for r in range(1, rounds):
+                d = mi.draw_layer(cfg, seed=seed + 100 * r, device=dev, with_raw=False)
+                qs.append(mi.plant_router_queries(self.kbar_r, d["planted"], d["q_r_noise"], cfg))
+            t["q_r_rounds"] = torch.stack(qs).contiguous()
+        kk = rounds * cfg.topk
         self.scores = e(cfg.batch, cfg.n_doc, dt=torch.float32)
-        self.ids = e(cfg.batch, cfg.topk, dt=torch.int32)
-        self.top = e(cfg.batch, cfg.topk, dt=torch.float32)
-        self.k_sel = e(cfg.batch, cfg.mem_len, cfg.heads_kv, cfg.dim)
-        self.v_sel = e(cfg.batch, cfg.mem_len, cfg.heads_kv, cfg.dim)
+        self.ids = e(cfg.batch, kk, dt=torch.int32)
+        self.top = e(cfg.batch, kk, dt=torch.float32)
+        self.k_sel = e(cfg.batch, rounds * cfg.mem_len, cfg.heads_kv, cfg.dim)
+        self.v_sel = e(cfg.batch, rounds * cfg.mem_len, cfg.heads_kv, cfg.dim)
         self.out = torch.empty_like(t["q"])
         self.lse = e(cfg.batch, cfg.heads_q, cfg.q_len, dt=torch.float32)
         u8 = lambda n: torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
@@ -300,7 +325,12 @@ class Step:
                                                           cfg.n_doc, cpd, torch.bfloat16))
         self.ws_topk = u8(msa.msa_topk_docs_workspace(cfg.batch, cfg.n_doc, cfg.topk))
         self.ws_attn = u8(msa.msa_sparse_attn_workspace(cfg.batch, cfg.q_len, cfg.heads_q, cfg.heads_kv,
-                                                        cfg.dim, cfg.mem_len, cfg.loc_len, torch.bfloat16))
+                                                        cfg.dim, rounds * cfg.mem_len, cfg.loc_len,
+                                                        torch.bfloat16))
+        if workload == "interleave":
+            self.ws_rounds = u8(msa.msa_route_rounds_workspace(rounds, cfg.batch, cfg.q_len, cfg.heads_kv,
+                                                               cfg.dim, cfg.n_doc, cpd, cfg.topk,
+                                                               torch.bfloat16))
         torch.cuda.synchronize()
 
     def _pool(self):
@@ -317,11 +347,17 @@ class Step:
             seq += [("pool", lambda: msa.msa_pool_chunks(t["k"], c, xbar=self.kbar)),
                     ("pool", lambda: msa.msa_pool_chunks(t["v"], c, xbar=self.vbar)),
                     ("pool", lambda: msa.msa_pool_chunks(t["k_r"], c, xbar=self.kbar_r, xbar_norm=self.knorm))]
+        if self.workload == "interleave":
+            seq += [("rounds", lambda: msa.msa_route_rounds(t["q_r_rounds"], self.kbar_r, self.knorm,
+                                                            cfg.chunks_per_doc, cfg.topk, topk_ids=self.ids,
+                                                            topk_scores=self.top, ws=self.ws_rounds))]
+        else:
+            seq += [
+                ("route", lambda: msa.msa_route_scores(t["q_r"], self.kbar_r, self.knorm, cfg.chunks_per_doc,
+                                                       doc_scores=self.scores, ws=self.ws_route)),
+                ("topk", lambda: msa.msa_topk_docs(self.scores, cfg.topk, topk_ids=self.ids,
+                                                   topk_scores=self.top, ws=self.ws_topk))]
         seq += [
-            ("route", lambda: msa.msa_route_scores(t["q_r"], self.kbar_r, self.knorm, cfg.chunks_per_doc,
-                                                   doc_scores=self.scores, ws=self.ws_route)),
-            ("topk", lambda: msa.msa_topk_docs(self.scores, cfg.topk, topk_ids=self.ids, topk_scores=self.top,
-                                               ws=self.ws_topk)),
             ("gather", lambda: msa.msa_gather_kv(self.kbar, self.vbar, self.ids, cfg.chunks_per_doc,
                                                  k_sel=self.k_sel, v_sel=self.v_sel)),
             ("attn", lambda: msa.msa_sparse_attn(t["q"], self.k_sel, self.v_sel, t["k_loc"], t["v_loc"],
@@ -469,7 +505,7 @@ def cpu_baseline(step, cfg, workload):
     """Time the float64 oracle on a bounded sample of the step and scale it up."""
     import numpy as np
     import torch
-    from oracle import pool_chunks_mean, route_scores, sparse_attention_rows, topk_docs
+    from oracle import pool_chunks_mean, route_scores, sparse_attention_rows, topk_docs, topk_docs_excluding
     try:
         from threadpoolctl import threadpool_info
         blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
@@ -492,16 +528,31 @@ def cpu_baseline(step, cfg, workload):
     n_route = 256
     sample = rng.choice(cfg.n_doc, n_route, replace=False)
     rows = torch.as_tensor((sample[:, None] * cpd + np.arange(cpd)).ravel(), device=step.kbar_r.device)
-    q_r, kb = f(step.t["q_r"]), f(step.kbar_r[rows])
-    t0 = time.perf_counter()
-    route_scores(q_r, kb, cpd)
-    secs += (time.perf_counter() - t0) * cfg.n_doc / n_route
-    parts.append(f"route all tokens vs {n_route}/{cfg.n_doc} docs")
-    sc = f(step.scores)
-    t0 = time.perf_counter()
-    topk_docs(sc, cfg.topk)
-    secs += time.perf_counter() - t0
-    parts.append("top-k whole")
+    kb = f(step.kbar_r[rows])
+    q_rounds = [step.t["q_r"]] if workload != "interleave" else list(step.t["q_r_rounds"])
+    for q_r in q_rounds:
+        q_r = f(q_r)
+        t0 = time.perf_counter()
+        route_scores(q_r, kb, cpd)
+        secs += (time.perf_counter() - t0) * cfg.n_doc / n_route
+    parts.append(f"route all tokens vs {n_route}/{cfg.n_doc} docs" +
+                 (f", each of {len(q_rounds)} rounds" if len(q_rounds) > 1 else ""))
+    if workload == "interleave":
+        # whole top-k of every round, on Gaussian scores of the same shape
+        sc = rng.standard_normal((cfg.batch, cfg.n_doc))
+        prev = np.empty((cfg.batch, 0), dtype=np.int64)
+        t0 = time.perf_counter()
+        for _ in q_rounds:
+            ids, _ = topk_docs_excluding(sc, cfg.topk, prev)
+            prev = np.concatenate([prev, ids], axis=1)
+        secs += time.perf_counter() - t0
+        parts.append("top-k excluding earlier rounds, whole, every round")
+    else:
+        sc = f(step.scores)
+        t0 = time.perf_counter()
+        topk_docs(sc, cfg.topk)
+        secs += time.perf_counter() - t0
+        parts.append("top-k whole")
     # gather is a copy; attention on sampled rows (uniform over (b, t, h))
     ks, vs = f(step.k_sel), f(step.v_sel)
     kl, vl, q = f(step.t["k_loc"]), f(step.t["v_loc"]), f(step.t["q"])
@@ -548,9 +599,11 @@ def main():
     import torch
     import msa_inputs as mi
     dev = "cuda:0"
-    cfg = mi.PREFILL if args.workload == "prefill" else mi.DECODE
-    print(f"[bench] building inputs for {cfg.name}", file=sys.stderr, flush=True)
-    step = Step(cfg, args.workload, args.seed, dev)
+    cfg = mi.DECODE if args.workload == "decode" else mi.PREFILL
+    rounds = INTERLEAVE_ROUNDS if args.workload == "interleave" else 1
+    name = cfg.name if rounds == 1 else f"interleave{rounds}-1M-bf16"
+    print(f"[bench] building inputs for {name}", file=sys.stderr, flush=True)
+    step = Step(cfg, args.workload, args.seed, dev, rounds=rounds)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     step.run(args.warmup, events=False)
@@ -567,8 +620,9 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
 
-    works = {"pool": None, "route": work_route(cfg), "topk": work_topk(cfg), "gather": work_gather(cfg),
-             "attn": work_attn(cfg)}
+    mem_cfg = dataclasses.replace(cfg, topk=rounds * cfg.topk)      # the memory all rounds gathered
+    works = {"pool": None, "route": work_route(cfg), "topk": work_topk(cfg), "gather": work_gather(mem_cfg),
+             "attn": work_attn(mem_cfg), "rounds": work_rounds(cfg, rounds)}
     per = {}
     counts = {}
     for stage, a, b in marks:
@@ -592,7 +646,9 @@ def main():
     tokens = cfg.batch * cfg.q_len
     online_ms = sum(stages[s]["ms_per_step"] for s in stages if s != "pool")
     rec = {
-        "metric": "query tokens/s at 1M-token memory (routing-scan GB/s + sparse-attn TFLOP/s in stages)",
+        "metric": ("query tokens/s at 1M-token memory (routing-scan GB/s + sparse-attn TFLOP/s in stages)"
+                   if rounds == 1 else
+                   f"query tokens/s at 1M-token memory with {rounds} routing rounds (Memory Interleave)"),
         "value": tokens / (ms_per_step / 1e3),
         "unit": "query tokens/s",
         "n_gpus": 1,
@@ -604,11 +660,14 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "n_docs": cfg.n_doc, "doc_len": cfg.doc_len, "chunk": cfg.chunk,
+        "config": {"workload": name, "n_docs": cfg.n_doc, "doc_len": cfg.doc_len, "chunk": cfg.chunk,
                    "batch": cfg.batch, "q_len": cfg.q_len, "loc_len": cfg.loc_len, "heads_q": cfg.heads_q,
-                   "heads_kv": cfg.heads_kv, "dim": cfg.dim, "topk": cfg.topk,
-                   "step": ("pool K,V,K_r -> route -> top-k -> gather -> attention" if args.workload == "prefill"
-                            else "route -> top-k -> gather -> split-KV attention")},
+                   "heads_kv": cfg.heads_kv, "dim": cfg.dim, "topk": cfg.topk, "rounds": rounds,
+                   "mem_len": rounds * cfg.mem_len,
+                   "step": {"prefill": "pool K,V,K_r -> route -> top-k -> gather -> attention",
+                            "decode": "route -> top-k -> gather -> split-KV attention",
+                            "interleave": f"(route -> top-k excluding earlier picks) x{rounds} -> gather -> "
+                                          "attention"}[args.workload]},
         "roofline": roof,
         "stages": stages,
         "online_tokens_per_s": tokens / (online_ms / 1e3),
