@@ -38,6 +38,7 @@ from .msa_oracle import (
     gather_kv,
     sparse_attention,
     sparse_attention_rows,
+    sparse_attention_backward,
 )
 
 __all__ = [
@@ -58,4 +59,5 @@ __all__ = [
     "gather_kv",
     "sparse_attention",
     "sparse_attention_rows",
+    "sparse_attention_backward",
 ]

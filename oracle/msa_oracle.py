@@ -380,3 +380,69 @@ def sparse_attention(q, k_sel, v_sel, k_loc, v_loc, scale=None):
                 o[b, t, h], lse[b, h, t] = sparse_attention_rows(
                     q[b, t, h], keys[:visible], vals[:visible], scale)
     return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Backward of the sparse attention (the method is trained end to end)
+# ---------------------------------------------------------------------------
+
+def sparse_attention_backward(q, k_sel, v_sel, k_loc, v_loc, d_out, scale=None):
+    """Gradients of :func:`sparse_attention` ([README] "Abstract" and the
+    Figure 1 caption: top-k selection is fused with sparse attention so that
+    the model stays end-to-end differentiable; [Card] "Architecture summary"
+    and "Training (CPT)": the router and adapters are trained through the
+    routed layers).
+
+    Given dL/do = ``d_out`` [B, T, H_q, d], for each (b, h) with KV head g and
+    each query row t over its visible keys (as in the forward):
+        p      = softmax(scale * q_t . keys^T)
+        dv_j  += p_j * dO_t                      (V of key j)
+        dp_j   = dO_t . v_j
+        ds_j   = p_j * (dp_j - sum_l p_l dp_l)   (softmax Jacobian)
+        dq_t   = scale * sum_j ds_j k_j
+        dk_j  += scale * ds_j * q_t
+    A KV head's gradients sum over the query heads of its group and over the
+    query tokens that see it.  Written per (b, h) as masked matrix products.
+
+    Returns float64 (dq [B,T,H_q,d], dk_sel [B,M,H_kv,d], dv_sel [B,M,H_kv,d],
+    dk_loc [B,L,H_kv,d], dv_loc [B,L,H_kv,d]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    ks = np.asarray(k_sel, dtype=np.float64)
+    vs = np.asarray(v_sel, dtype=np.float64)
+    kl = np.asarray(k_loc, dtype=np.float64)
+    vl = np.asarray(v_loc, dtype=np.float64)
+    do = np.asarray(d_out, dtype=np.float64)
+    b_, t_, hq, d = q.shape
+    m_len, l_len, hkv = ks.shape[1], kl.shape[1], ks.shape[2]
+    if hq % hkv != 0:
+        raise ValueError("query heads must be a multiple of KV heads")
+    if l_len < t_:
+        raise ValueError("local KV must hold at least the query tokens")
+    if do.shape != q.shape:
+        raise ValueError("d_out must have the query's shape")
+    group = hq // hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    n_keys = m_len + l_len
+    # visible[t, j]: memory rows always; local row i when i <= L - T + t
+    j = np.arange(n_keys)
+    t = np.arange(t_)
+    visible = (j[None, :] < m_len) | ((j[None, :] - m_len) <= (l_len - t_ + t)[:, None])
+    dq = np.zeros_like(q)
+    dkeys = np.zeros((b_, n_keys, hkv, d))
+    dvals = np.zeros((b_, n_keys, hkv, d))
+    for b in range(b_):
+        for h in range(hq):
+            g = h // group
+            keys = np.concatenate([ks[b, :, g], kl[b, :, g]], axis=0)    # [n_keys, d]
+            vals = np.concatenate([vs[b, :, g], vl[b, :, g]], axis=0)
+            logits = np.where(visible, scale * (q[b, :, h] @ keys.T), -np.inf)
+            p = np.exp(logits - logits.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)                               # [T, n_keys]
+            dp = do[b, :, h] @ vals.T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dq[b, :, h] = scale * (ds @ keys)
+            dkeys[b, :, g] += scale * (ds.T @ q[b, :, h])
+            dvals[b, :, g] += p.T @ do[b, :, h]
+    return dq, dkeys[:, :m_len], dvals[:, :m_len], dkeys[:, m_len:], dvals[:, m_len:]
