@@ -1,6 +1,6 @@
 """Benchmark of the MSA routed-layer hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode|interleave|encode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode|interleave|backward|encode]
                     [--no-cpu-baseline]
 
 A step is one pass of the whole hot path over one batch of synthetic input
@@ -17,6 +17,10 @@ already resident in HBM:
            keeps the top-16 documents no earlier round took; the 48 documents'
            memory, 384 pooled rows, then joins the prefill attention):
       route+top-k x3 -> gather -> attention (the bank is pooled outside the step)
+  backward (training step of the routed layer's attention at the prefill
+           shapes: 2048 tokens, 128 gathered memory rows, 2048 local rows,
+           32/8 heads): attention forward -> attention backward (dq; dk, dv of
+           the memory and local rows)
   encode  (offline encoder: 2048 documents of 256..768 tokens, ~1M tokens,
            8 KV heads x 128, bf16): chunk offsets -> encode K (document-wise
            RoPE, base 1e6) -> encode V -> encode K_r (+ norms)
@@ -62,7 +66,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", choices=["prefill", "decode", "interleave", "encode"], default="prefill")
+    p.add_argument("--workload", choices=["prefill", "decode", "interleave", "backward", "encode"], default="prefill")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     # profiling helpers (see "Profiles" in the module docstring)
@@ -154,6 +158,8 @@ STAGE_KERNELS = {
                "gather": ("gather", "gather.hip"), "attn": ("attn_decode", "attn_decode.hip")},
     "interleave": {"rounds": ("route_", "route.hip"), "gather": ("gather", "gather.hip"),
                    "attn": ("attn_prefill", "attn_prefill.hip")},
+    "backward": {"attn": ("attn_prefill", "attn_prefill.hip"), "attn_bwd": ("attn_bwd", "attn_backward.hip")},
+    # (the backward stage is two kernels, dq then dk/dv; its entry covers both)
     "encode": {"offsets": ("chunk_offsets", "encode.hip"), "encode": ("encode_kernel", "encode.hip")},
     # (both encode launches share one kernel template; the traffic entry covers their average)
 }
@@ -454,6 +460,133 @@ class EncodeStep:
                 "seconds_per_step": secs}
 
 
+class BackwardStep:
+    """Attention forward + backward at the prefill layer's shapes (a training
+    step of the routed layer's attention; the gathered memory rows are drawn
+    directly, N(0,1)/sqrt(128) like every other value, and dL/dO is N(0,1))."""
+
+    def __init__(self, seed, dev):
+        import torch
+        import msa_inputs as mi
+        import routed_sparse_attention_msa_amd as msa
+        self.torch, self.msa, self.cfg = torch, msa, mi.PREFILL
+        cfg = self.cfg
+        t = mi.draw_layer(cfg, seed=seed, device=dev, with_raw=False)
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed + 7)
+        mem = (cfg.batch, cfg.mem_len, cfg.heads_kv, cfg.dim)
+        self.q, self.k_loc, self.v_loc = t["q"], t["k_loc"], t["v_loc"]
+        self.k_sel = (torch.randn(mem, generator=g, device=dev) * cfg.value_scale).to(torch.bfloat16)
+        self.v_sel = (torch.randn(mem, generator=g, device=dev) * cfg.value_scale).to(torch.bfloat16)
+        self.d_out = torch.randn(self.q.shape, generator=g, device=dev).to(torch.bfloat16)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty((cfg.batch, cfg.heads_q, cfg.q_len), dtype=torch.float32, device=dev)
+        self.grads = (torch.empty_like(self.q), torch.empty_like(self.k_sel), torch.empty_like(self.v_sel),
+                      torch.empty_like(self.k_loc), torch.empty_like(self.v_loc))
+        u8 = lambda n: torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+        self.ws = u8(msa.msa_sparse_attn_backward_workspace(cfg.batch, cfg.q_len, cfg.heads_q, cfg.heads_kv,
+                                                            cfg.dim, cfg.mem_len, cfg.loc_len, torch.bfloat16))
+        torch.cuda.synchronize()
+
+    def calls(self):
+        msa = self.msa
+        return [("attn", lambda: msa.msa_sparse_attn(self.q, self.k_sel, self.v_sel, self.k_loc, self.v_loc,
+                                                     out=self.out, lse=self.lse)),
+                ("attn_bwd", lambda: msa.msa_sparse_attn_backward(self.q, self.k_sel, self.v_sel, self.k_loc,
+                                                                  self.v_loc, self.out, self.lse, self.d_out,
+                                                                  grads=self.grads, ws=self.ws))]
+
+    run = Step.run
+
+    def work(self, stage):
+        fwd = work_attn(self.cfg)
+        if stage == "attn":
+            return fwd
+        # flash-attention accounting: S recomputed, dP, dQ, dK, dV = 2.5 x the forward's products;
+        # bytes: q, k, v, o, dO, lse read, dq, dk, dv written
+        c = self.cfg
+        row_kv = c.heads_kv * c.dim * 2
+        q_b = c.batch * c.q_len * c.heads_q * c.dim * 2
+        kv_b = 2 * c.batch * (c.mem_len + c.loc_len) * row_kv
+        b = 4 * q_b + 2 * kv_b + c.batch * c.heads_q * c.q_len * 4
+        return {"bound": "mfma", "bytes": b, "flops": 2.5 * fwd["flops"]}
+
+    def cpu_baseline(self):
+        import numpy as np
+        from oracle import sparse_attention_backward
+        try:
+            from threadpoolctl import threadpool_info
+            blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:  # pragma: no cover
+            blas = 1
+        c = self.cfg
+        f = lambda x: x.detach().float().cpu().double().numpy()
+        # one KV group (its 4 query heads) of the 8, scaled to all of them
+        gs, hs = slice(0, 1), slice(0, c.heads_q // c.heads_kv)
+        args = [f(self.q[:, :, hs]), f(self.k_sel[:, :, gs]), f(self.v_sel[:, :, gs]), f(self.k_loc[:, :, gs]),
+                f(self.v_loc[:, :, gs]), f(self.d_out[:, :, hs])]
+        t0 = time.perf_counter()
+        sparse_attention_backward(*args, scale=1.0 / math.sqrt(c.dim))
+        secs = (time.perf_counter() - t0) * c.heads_kv
+        tokens = c.batch * c.q_len
+        return {"value": tokens / secs, "unit": "query tokens/s", "cores": int(blas), "kind": "oracle",
+                "sample": f"backward of 1 of {c.heads_kv} KV groups (all tokens), scaled to all groups; "
+                          "the forward not timed",
+                "seconds_per_step": secs}
+
+
+def main_backward(args):
+    import torch
+    dev = "cuda:0"
+    print("[bench] building inputs for backward-1M-layer-bf16", file=sys.stderr, flush=True)
+    step = BackwardStep(args.seed, dev)
+    step.run(args.warmup, events=False)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    marks = step.run(args.steps, events=True)
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    stages = stage_summary(step, marks, args.steps)
+    dom = max(stages, key=lambda k: stages[k]["ms_per_step"])
+    roof = {k: stages[dom][k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+    roof.update({"kernel": dom, "avg_launch_ms": stages[dom]["avg_launch_ms"],
+                 "traffic": measured_traffic("backward", dom)})
+    c = step.cfg
+    tokens = c.batch * c.q_len
+    rec = {
+        "metric": "query tokens/s of the routed layer's attention forward + backward (training step)",
+        "value": tokens / (ms_per_step / 1e3), "unit": "query tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "backward-1M-layer-bf16", "batch": c.batch, "q_len": c.q_len,
+                   "loc_len": c.loc_len, "mem_len": c.mem_len, "heads_q": c.heads_q, "heads_kv": c.heads_kv,
+                   "dim": c.dim, "step": "attention forward -> attention backward"},
+        "roofline": roof, "stages": stages,
+        "cpu_baseline": None if args.no_cpu_baseline else step.cpu_baseline(),
+    }
+    print(json.dumps(rec))
+
+
+def stage_summary(step, marks, steps):
+    per, counts = {}, {}
+    for stage, a, b in marks:
+        per[stage] = per.get(stage, 0.0) + a.elapsed_time(b)
+        counts[stage] = counts.get(stage, 0) + 1
+    stages = {}
+    for stage in per:
+        avg = per[stage] / counts[stage]
+        entry = roofline_entry(step.work(stage), avg)
+        entry.update({"avg_launch_ms": avg, "launches_per_step": counts[stage] // steps,
+                      "ms_per_step": per[stage] / steps})
+        stages[stage] = entry
+    return stages
+
+
 def main_encode(args):
     import torch
     dev = "cuda:0"
@@ -595,6 +728,9 @@ def main():
         sys.exit(2)
     if args.workload == "encode":
         main_encode(args)
+        return
+    if args.workload == "backward":
+        main_backward(args)
         return
     import torch
     import msa_inputs as mi

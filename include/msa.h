@@ -263,6 +263,35 @@ msa_status msa_sparse_attn(const void* q, const void* k_sel, const void* v_sel, 
                            float scale, msa_dtype dt, void* out, float* lse, void* ws,
                            size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Backward of the sparse attention (MSA README "Abstract" and Figure 1
+ *     caption: top-k selection fused with a sparse attention that stays
+ *     end-to-end differentiable; model card "Training (CPT)": the router and
+ *     adapters train through the routed layers).
+ *
+ * Given the forward's inputs, its output `out` and log-sum-exp `lse` (from
+ * msa_sparse_attn with the same scale), and d_out = dL/d out, writes
+ *   d_q    [batch, q_len, heads_q, dim]
+ *   d_k_sel, d_v_sel [batch, mem_len, heads_kv, dim]   (NULL iff mem_len == 0)
+ *   d_k_loc, d_v_loc [batch, loc_len, heads_kv, dim]
+ * all in dtype dt (float32 accumulation).  With P the forward's softmax over
+ * the visible keys and D_t = sum_d d_out[t,d] * out[t,d]:
+ *   dP = d_out V^T,  dS = P o (dP - D),  d_q = scale dS K,
+ *   d_k = scale dS^T Q,  d_v = P^T d_out,
+ * a KV head's gradients summing over its query heads and the tokens that see
+ * it.  Rows no token sees get zero gradients.  ws: msa_sparse_attn_backward_
+ * workspace() bytes (D per query row).  Deterministic (no atomics).
+ * ---------------------------------------------------------------------- */
+msa_status msa_sparse_attn_backward_workspace(int32_t batch, int32_t q_len, int32_t heads_q,
+                                              int32_t heads_kv, int32_t dim, int32_t mem_len,
+                                              int32_t loc_len, msa_dtype dt, size_t* bytes);
+msa_status msa_sparse_attn_backward(const void* q, const void* k_sel, const void* v_sel, int32_t mem_len,
+                                    const void* k_loc, const void* v_loc, int32_t loc_len, const void* out,
+                                    const void* d_out, const float* lse, int32_t batch, int32_t q_len,
+                                    int32_t heads_q, int32_t heads_kv, int32_t dim, float scale,
+                                    msa_dtype dt, void* d_q, void* d_k_sel, void* d_v_sel, void* d_k_loc,
+                                    void* d_v_loc, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,6 +12,7 @@ of ``include/msa.h``; this package is its thin Python binding:
     msa_route_rounds         multi-round routing (Memory Interleave)
     msa_gather_kv            S4  gather (or host-tier fetch) of the selected pooled K/V
     msa_sparse_attn          S5/S6 sparse GQA attention (prefill and decode)
+    msa_sparse_attn_backward its gradients (training through the routed layer)
 """
 
 from ._lib import (  # noqa: F401
@@ -27,6 +28,8 @@ from ._lib import (  # noqa: F401
     msa_route_scores,
     msa_route_scores_workspace,
     msa_sparse_attn,
+    msa_sparse_attn_backward,
+    msa_sparse_attn_backward_workspace,
     msa_sparse_attn_workspace,
     msa_topk_docs,
     msa_topk_docs_excluding,

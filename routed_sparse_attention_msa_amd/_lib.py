@@ -53,6 +53,12 @@ SIGNATURES = {
     "msa_sparse_attn": (_STATUS, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
                                   c_int32, c_int32, c_int32, c_int32, c_int32, c_float, c_int,
                                   c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "msa_sparse_attn_backward_workspace": (_STATUS, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                                     c_int32, c_int, POINTER(c_size_t)]),
+    "msa_sparse_attn_backward": (_STATUS, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
+                                           c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
+                                           c_int32, c_float, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                           c_void_p, c_void_p, c_size_t, c_void_p]),
 }
 
 
@@ -427,3 +433,59 @@ def msa_sparse_attn(q, k_sel, v_sel, k_loc, v_loc, scale=None, out=None, lse=Non
                                  _dtype_code(q), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
                                  _stream(q.device)))
     return out, lse
+
+
+def msa_sparse_attn_backward_workspace(batch, q_len, heads_q, heads_kv, dim, mem_len, loc_len, dtype):
+    n = c_size_t(0)
+    code = MSA_F32 if dtype == torch.float32 else MSA_BF16
+    _check(lib().msa_sparse_attn_backward_workspace(batch, q_len, heads_q, heads_kv, dim, mem_len, loc_len,
+                                                    code, ctypes.byref(n)))
+    return n.value
+
+
+def msa_sparse_attn_backward(q, k_sel, v_sel, k_loc, v_loc, out, lse, d_out, scale=None, grads=None, ws=None):
+    """Gradients of :func:`msa_sparse_attn` given its output ``out``, its ``lse`` (same scale) and
+    ``d_out`` = dL/d out: returns (d_q, d_k_sel, d_v_sel, d_k_loc, d_v_loc), d_k_sel/d_v_sel None when
+    there are no memory rows.  ``grads`` may hold preallocated outputs in that order."""
+    _dev(q, "q", ndim=4)
+    _dev(k_loc, "k_loc", dtype=q.dtype, ndim=4)
+    _dev(v_loc, "v_loc", dtype=q.dtype, ndim=4)
+    _dev(out, "out", dtype=q.dtype, ndim=4)
+    _dev(d_out, "d_out", dtype=q.dtype, ndim=4)
+    _dev(lse, "lse", dtype=torch.float32, ndim=3)
+    batch, q_len, heads_q, dim = q.shape
+    loc_len, heads_kv = k_loc.shape[1], k_loc.shape[2]
+    if k_sel is None:
+        mem_len = 0
+    else:
+        _dev(k_sel, "k_sel", dtype=q.dtype, ndim=4)
+        _dev(v_sel, "v_sel", dtype=q.dtype, ndim=4)
+        mem_len = k_sel.shape[1]
+        if k_sel.shape != (batch, mem_len, heads_kv, dim) or v_sel.shape != k_sel.shape:
+            raise ValueError("k_sel/v_sel shape mismatch")
+    if k_loc.shape != (batch, loc_len, heads_kv, dim) or v_loc.shape != k_loc.shape:
+        raise ValueError("k_loc/v_loc shape mismatch")
+    if out.shape != q.shape or d_out.shape != q.shape or lse.shape != (batch, heads_q, q_len):
+        raise ValueError("out, d_out and lse must match the query")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dim)
+    if grads is None:
+        grads = (torch.empty_like(q),
+                 torch.empty_like(k_sel) if mem_len else None, torch.empty_like(v_sel) if mem_len else None,
+                 torch.empty_like(k_loc), torch.empty_like(v_loc))
+    d_q, d_ks, d_vs, d_kl, d_vl = grads
+    for name, t, ref in (("d_q", d_q, q), ("d_k_loc", d_kl, k_loc), ("d_v_loc", d_vl, v_loc),
+                         ("d_k_sel", d_ks, k_sel), ("d_v_sel", d_vs, v_sel)):
+        if ref is None:
+            continue
+        _dev(t, name, dtype=q.dtype)
+        if t.shape != ref.shape:
+            raise ValueError(f"{name} must have shape {tuple(ref.shape)}")
+    nbytes = msa_sparse_attn_backward_workspace(batch, q_len, heads_q, heads_kv, dim, mem_len, loc_len, q.dtype)
+    ws, ws_bytes = _workspace(nbytes, q.device, ws)
+    _check(lib().msa_sparse_attn_backward(_ptr(q), _ptr(k_sel), _ptr(v_sel), mem_len, _ptr(k_loc), _ptr(v_loc),
+                                          loc_len, _ptr(out), _ptr(d_out), _ptr(lse), batch, q_len, heads_q,
+                                          heads_kv, dim, float(scale), _dtype_code(q), _ptr(d_q), _ptr(d_ks),
+                                          _ptr(d_vs), _ptr(d_kl), _ptr(d_vl), _ptr(ws), ws_bytes,
+                                          _stream(q.device)))
+    return d_q, d_ks, d_vs, d_kl, d_vl

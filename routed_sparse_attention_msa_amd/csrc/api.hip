@@ -471,4 +471,41 @@ msa_status msa_sparse_attn(const void* q, const void* k_sel, const void* v_sel, 
                     "msa_sparse_attn launch");
 }
 
+msa_status msa_sparse_attn_backward_workspace(int32_t batch, int32_t q_len, int32_t heads_q,
+                                              int32_t heads_kv, int32_t dim, int32_t mem_len,
+                                              int32_t loc_len, msa_dtype dt, size_t* bytes) {
+  msa_status st = check_attn(batch, q_len, heads_q, heads_kv, dim, mem_len, loc_len, dt);
+  if (st != MSA_OK) return st;
+  CHECK_ARG(bytes != nullptr, "bytes is null");
+  *bytes = msa::attn_backward_workspace_bytes(batch, q_len, heads_q, heads_kv, dim, mem_len, loc_len, dt);
+  return MSA_OK;
+}
+
+msa_status msa_sparse_attn_backward(const void* q, const void* k_sel, const void* v_sel, int32_t mem_len,
+                                    const void* k_loc, const void* v_loc, int32_t loc_len, const void* out,
+                                    const void* d_out, const float* lse, int32_t batch, int32_t q_len,
+                                    int32_t heads_q, int32_t heads_kv, int32_t dim, float scale,
+                                    msa_dtype dt, void* d_q, void* d_k_sel, void* d_v_sel, void* d_k_loc,
+                                    void* d_v_loc, void* ws, size_t ws_bytes, void* stream) {
+  msa_status st = check_attn(batch, q_len, heads_q, heads_kv, dim, mem_len, loc_len, dt);
+  if (st != MSA_OK) return st;
+  CHECK_ARG(q && k_loc && v_loc && out && d_out && lse && d_q && d_k_loc && d_v_loc, "null tensor pointer");
+  CHECK_ARG(mem_len == 0 || (k_sel && v_sel && d_k_sel && d_v_sel),
+            "k_sel/v_sel and their gradients required when mem_len > 0");
+  CHECK_ARG(aligned16(q) && aligned16(k_loc) && aligned16(v_loc) && aligned16(out) && aligned16(d_out) &&
+                aligned16(lse) && aligned16(d_q) && aligned16(d_k_loc) && aligned16(d_v_loc) &&
+                (mem_len == 0 || (aligned16(k_sel) && aligned16(v_sel) && aligned16(d_k_sel) &&
+                                  aligned16(d_v_sel))),
+            "tensors must be 16-byte aligned");
+  CHECK_ARG(scale == scale && scale > 0.f, "scale must be positive");
+  const size_t need = msa::attn_backward_workspace_bytes(batch, q_len, heads_q, heads_kv, dim, mem_len, loc_len, dt);
+  CHECK_ARG(ws_bytes >= need, "workspace too small (%zu < %zu bytes)", ws_bytes, need);
+  CHECK_ARG(ws != nullptr && aligned16(ws), "workspace pointer missing or misaligned");
+  return hip_status(msa::launch_attn_backward(q, k_sel, v_sel, mem_len, k_loc, v_loc, loc_len, out, d_out,
+                                              lse, batch, q_len, heads_q, heads_kv, dim, scale, dt, d_q,
+                                              d_k_sel, d_v_sel, d_k_loc, d_v_loc, ws,
+                                              static_cast<hipStream_t>(stream)),
+                    "msa_sparse_attn_backward launch");
+}
+
 }  // extern "C"

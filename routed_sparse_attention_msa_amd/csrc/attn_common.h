@@ -1,0 +1,76 @@
+// Shared pieces of the bf16 MFMA attention kernels (forward and backward):
+// the 32x32x16 MFMA, the accumulator row map, the LDS layouts of K rows and
+// of transposed operand groups, bf16 packing and buffer-resource loads.
+#pragma once
+
+#include "internal.h"
+
+namespace msa {
+namespace attn {
+
+constexpr int kD = 128;                 // head dim of the MFMA kernels
+constexpr int kVGStride = 144;          // 16 B units per operand-group row: 128 d + one pad unit per 8
+constexpr int kKPitch = 272;            // bytes per row in LDS: 256 + 16 pad (conflict-free reads)
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+// Row of accumulator element i held by lane half hf (the column is the lane % 32).
+__device__ __forceinline__ int acc_row(int i, int hf) { return 8 * (i >> 2) + 4 * hf + (i & 3); }
+// Transposed operand groups: group G = 4*kb + 2*s2 + hf holds rows
+// 32kb + 16s2 + 4hf + {0..3, 8..11} of a tile, one 16-byte unit (8 rows at
+// one d) per d, so that a lane's 8 contraction values of one MFMA are one read.
+__device__ __forceinline__ int vunit(int grp, int d) { return (grp * kVGStride + d + (d >> 3)) * 16; }
+// First row of transposed-staging task c (4 rows, one 8-d block).
+__device__ __forceinline__ int vtask_row0(int c) {
+  const int grp = c >> 5, half = (c >> 4) & 1;
+  return 32 * (grp >> 2) + 16 * ((grp >> 1) & 1) + 4 * (grp & 1) + 8 * half;
+}
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ uint32_t perm_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2v v = {(__bf16)lo, (__bf16)hi};   // v_cvt_pk_bf16_f32, round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Store four rows (one 8-d block each: r[0..3]) of a tile into the transposed
+// operand groups: unit (grp, d) gets rows {4 of them} as 8-byte halves.
+__device__ __forceinline__ void store_transposed(uint8_t* base, int grp, int half, int dblk, const u32x4 (&r)[4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {   // d = 8*dblk + 2e and 2e + 1
+    uint2 lo, hi;
+    lo.x = perm_lo(r[0][e], r[1][e]);
+    lo.y = perm_lo(r[2][e], r[3][e]);
+    hi.x = perm_hi(r[0][e], r[1][e]);
+    hi.y = perm_hi(r[2][e], r[3][e]);
+    *reinterpret_cast<uint2*>(base + vunit(grp, 8 * dblk + 2 * e) + 8 * half) = lo;
+    *reinterpret_cast<uint2*>(base + vunit(grp, 8 * dblk + 2 * e + 1) + 8 * half) = hi;
+  }
+}
+
+// Memory rows and local rows of one (sequence, KV head), each behind a buffer
+// resource based at the sequence's first row and sized to its rows: a row
+// past the end reads as zeros.
+struct KVRows {
+  __amdgpu_buffer_rsrc_t sel, loc;
+  uint32_t rs;                       // row stride in bytes (heads_kv * 256)
+  // 16 bytes at byte voff of row `row0` of the memory (mem) or local rows; the
+  // choice is uniform, so it is a scalar select and the load has no branch.
+  __device__ __forceinline__ u32x4 load(bool mem, int row0, uint32_t voff) const {
+    return bload(mem ? sel : loc, voff, (uint32_t)row0 * rs);
+  }
+};
+
+}  // namespace attn
+}  // namespace msa

@@ -39,57 +39,19 @@
 // never mixes the two); tiles fully below every query's causal limit skip
 // the mask, tiles beyond the last query's limit are never loaded.
 // Workgroups are issued longest-first.
-#include "internal.h"
+#include "attn_common.h"
 
 namespace msa {
 namespace {
 
-constexpr int kD = 128;
+using namespace attn;
+
 constexpr int kKT = 64;                 // keys per LDS tile
-constexpr int kVGStride = 144;          // 16 B units per V group row: 128 d + one pad unit per 8
-constexpr int kKPitch = 272;            // bytes per K row in LDS: 256 + 16 pad (conflict-free reads)
-constexpr uint32_t kRsrcWord3 = 0x00020000u;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.f;  // log2 headroom of the lazy running max
 
 struct PrefillSmem {
   uint8_t k[2][kKT * kKPitch];            // [key][256 B + pad]
   uint8_t v[2][8 * kVGStride * 16];       // [group][d + d/8][8 bf16]
-};
-
-__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
-__device__ __forceinline__ int acc_row(int i, int hf) { return 8 * (i >> 2) + 4 * hf + (i & 3); }
-// V group G = 4*kb + 2*s2 + hf holds keys 32kb + 16s2 + 4hf + {0..3, 8..11} of the tile.
-__device__ __forceinline__ int vunit(int grp, int d) { return (grp * kVGStride + d + (d >> 3)) * 16; }
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ uint32_t perm_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
-__device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
-
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const bf16x2v v = {(__bf16)lo, (__bf16)hi};   // v_cvt_pk_bf16_f32, round to nearest even
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-
-// Memory rows and local rows of one (sequence, KV head), each behind a buffer
-// resource based at the sequence's first row and sized to its rows: a row
-// past the end reads as zeros.
-struct KVRows {
-  __amdgpu_buffer_rsrc_t sel, loc;
-  uint32_t rs;                       // row stride in bytes (heads_kv * 256)
-  // 16 bytes at byte voff of row `row0` of the memory (mem) or local rows; the
-  // choice is uniform, so it is a scalar select and the load has no branch.
-  __device__ __forceinline__ u32x4 load(bool mem, int row0, uint32_t voff) const {
-    return bload(mem ? sel : loc, voff, (uint32_t)row0 * rs);
-  }
 };
 
 template <int NW, int SPLIT>
@@ -173,11 +135,6 @@ __global__ __launch_bounds__(NW * 64 * SPLIT, SPLIT == 1 && NW == 4 ? 2 : 1) voi
   const int krow0 = tid >> 4;
   const uint32_t k_in_row = goff + (tid & 15) * 16;
   const uint32_t kvoff = (uint32_t)krow0 * rs + k_in_row;
-  auto vtask_row0 = [&](int i) {
-    const int c = tid + kThreads * i;
-    const int grp = c >> 5, half = (c >> 4) & 1;
-    return 32 * (grp >> 2) + 16 * ((grp >> 1) & 1) + 4 * (grp & 1) + 8 * half;
-  };
   const uint32_t v_in_row = goff + (tid & 15) * 16;   // d-block = c % 16 = tid % 16
   u32x4 pk[kKChunks], pv[kVTasks][4];
   // Branch-free: rows past the block's needs are loaded too (they exist or
@@ -190,7 +147,7 @@ __global__ __launch_bounds__(NW * 64 * SPLIT, SPLIT == 1 && NW == 4 ? 2 : 1) voi
     for (int i = 0; i < kKChunks; ++i) pk[i] = kr.load(mem, row0 + kKRowStep * i, kvoff);
 #pragma unroll
     for (int i = 0; i < kVTasks; ++i) {
-      const uint32_t voff = (uint32_t)vtask_row0(i) * rs + v_in_row;
+      const uint32_t voff = (uint32_t)vtask_row0(tid + kThreads * i) * rs + v_in_row;
 #pragma unroll
       for (int j = 0; j < 4; ++j) pv[i][j] = vr.load(mem, row0 + j, voff);
     }

@@ -132,4 +132,12 @@ hipError_t launch_attn(const void* q, const void* k_sel, const void* v_sel, int 
                        int heads_q, int heads_kv, int dim, float scale, msa_dtype dt, void* out,
                        float* lse, void* ws, hipStream_t s);
 
+size_t attn_backward_workspace_bytes(int batch, int q_len, int heads_q, int heads_kv, int dim, int mem_len,
+                                     int loc_len, msa_dtype dt);
+hipError_t launch_attn_backward(const void* q, const void* k_sel, const void* v_sel, int mem_len,
+                                const void* k_loc, const void* v_loc, int loc_len, const void* out,
+                                const void* d_out, const float* lse, int batch, int q_len, int heads_q,
+                                int heads_kv, int dim, float scale, msa_dtype dt, void* dq, void* dk_sel,
+                                void* dv_sel, void* dk_loc, void* dv_loc, void* ws, hipStream_t s);
+
 }  // namespace msa
