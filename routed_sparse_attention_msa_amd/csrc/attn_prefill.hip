@@ -82,8 +82,18 @@ __global__ __launch_bounds__(NW * 64 * SPLIT, SPLIT == 1 && NW == 4 ? 2 : 1) voi
   const int g = bid % heads_kv;
   bid /= heads_kv;
   const int b = bid % batch;
-  const int tb = n_tblk - 1 - bid / batch;
+  const int pair = bid / batch;
   const int h = g * group + hs * NW + wave;
+  // A workgroup takes the token block n_tblk-1-pair (the longest causal rows)
+  // and then its mirror block `pair` (the shortest), so every workgroup has
+  // about the same number of key tiles and one round of workgroups finishes
+  // together.
+  for (int pass = 0; pass < 2; ++pass) {
+  const int tb = pass == 0 ? n_tblk - 1 - pair : pair;
+  if (pass == 1) {
+    if (tb == n_tblk - 1 - pair) break;         // odd block count: the middle block is alone
+    __syncthreads();                            // the first block's merge reads are done
+  }
   const int t0 = tb * 32;
   const int t = t0 + cl;                        // this lane's query token
   const bool t_ok = t < q_len;
@@ -223,18 +233,18 @@ __global__ __launch_bounds__(NW * 64 * SPLIT, SPLIT == 1 && NW == 4 ? 2 : 1) voi
         for (int i = 0; i < 16; ++i)
           if (kappa0 + kb * 32 + acc_row(i, hf) >= lim) s[kb][i] = -INFINITY;
     }
-    // three-input max tree (v_max3): 16 instructions for the 32 scores
-    float mx[4];
+    // three-input max tree (v_max3) over the 32 scores, two chains, then the
+    // other lane half
+    float mx[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int kb = j >> 1, i0 = 8 * (j & 1);
-      float a = fmaxf(fmaxf(s[kb][i0], s[kb][i0 + 1]), s[kb][i0 + 2]);
-      a = fmaxf(fmaxf(a, s[kb][i0 + 3]), s[kb][i0 + 4]);
-      a = fmaxf(fmaxf(a, s[kb][i0 + 5]), s[kb][i0 + 6]);
-      mx[j] = fmaxf(a, s[kb][i0 + 7]);
+    for (int kb = 0; kb < 2; ++kb) {
+      float a = max3(s[kb][0], s[kb][1], s[kb][2]);
+#pragma unroll
+      for (int i = 3; i < 15; i += 2) a = max3(a, s[kb][i], s[kb][i + 1]);
+      mx[kb] = a;
     }
-    float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m4 = max3(mx[0], mx[1], s[0][15]);
+    const float mt = half_swap_max(max3(m4, s[1][15], s[1][15]));
     // Lazy running max: it moves only when a score exceeds it by more than
     // kLazy / scale_log2 (probabilities then stay <= 2^kLazy, harmless in
     // float32), so the O^T rescale below is rare after the first tiles.
@@ -245,7 +255,7 @@ __global__ __launch_bounds__(NW * 64 * SPLIT, SPLIT == 1 && NW == 4 ? 2 : 1) voi
     m = m_new;
     const float off = m_new == -INFINITY ? 0.f : -m_new * scale_log2;
     // probabilities (float32 row sum, two chains), rounded to bf16 for PV
-    float lsum2[2] = {0.f, 0.f};
+    float lsum2[2] = {-0.f, -0.f};   // (-0 is the additive identity: no add of zero)
     bf16x8 pf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -302,8 +312,7 @@ __global__ __launch_bounds__(NW * 64 * SPLIT, SPLIT == 1 && NW == 4 ? 2 : 1) voi
       for (int i = 0; i < 16; ++i) mg[(2 + db * 16 + i) * 64 + lane] = o[db][i];
   }
   __syncthreads();
-  if (part == 1) return;
-  {
+  if (part == 0) {
     const float m1 = mg[lane], l1 = mg[64 + lane];
     const float mm = fmaxf(m, m1);
     const float a0 = fast_exp2((m - mm) * scale_log2);
@@ -318,8 +327,8 @@ __global__ __launch_bounds__(NW * 64 * SPLIT, SPLIT == 1 && NW == 4 ? 2 : 1) voi
   }
 
 
-  const float l_tot = l + __shfl_xor(l, 32);
-  if (!t_ok) return;
+  const float l_tot = half_swap_sum(l);
+  if (part == 0 && t_ok) {
   const float inv_l = 1.f / l_tot;
   uint16_t* orow = out + (((size_t)b * q_len + t) * heads_q + h) * kD;
 #pragma unroll
@@ -334,6 +343,8 @@ __global__ __launch_bounds__(NW * 64 * SPLIT, SPLIT == 1 && NW == 4 ? 2 : 1) voi
     }
   if (lse != nullptr && hf == 0)
     lse[((size_t)b * heads_q + h) * q_len + t] = (m * scale_log2 + __log2f(l_tot)) * kLn2;
+  }
+  }  // pass
 }
 
 }  // namespace
@@ -352,7 +363,7 @@ hipError_t launch_attn_prefill(const void* q, const void* k_sel, const void* v_s
   const int group = heads_q / heads_kv;
   const int nw = group % 4 == 0 ? 4 : group;
   const int n_tblk = (q_len + 31) / 32;
-  const unsigned grid = (unsigned)(n_tblk * batch * heads_kv * (group / nw));
+  const unsigned grid = (unsigned)((n_tblk + 1) / 2 * batch * heads_kv * (group / nw));
   static const hipError_t attr = [] {
     hipError_t e = hipSuccess;
     auto set = [&](auto kern, size_t bytes) {
