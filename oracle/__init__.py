@@ -39,6 +39,8 @@ from .msa_oracle import (
     sparse_attention,
     sparse_attention_rows,
     sparse_attention_backward,
+    gated_delta_rule,
+    inject_states,
 )
 
 __all__ = [
@@ -60,4 +62,6 @@ __all__ = [
     "sparse_attention",
     "sparse_attention_rows",
     "sparse_attention_backward",
+    "gated_delta_rule",
+    "inject_states",
 ]

@@ -446,3 +446,62 @@ def sparse_attention_backward(q, k_sel, v_sel, k_loc, v_loc, d_out, scale=None):
             dkeys[b, :, g] += scale * (ds.T @ q[b, :, h])
             dvals[b, :, g] += p.T @ do[b, :, h]
     return dq, dkeys[:, :m_len], dvals[:, :m_len], dkeys[:, m_len:], dvals[:, m_len:]
+
+
+# ---------------------------------------------------------------------------
+# Linear-layer variant: document states injected as the initial state
+# ---------------------------------------------------------------------------
+
+def gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None):
+    """Gated delta rule over a sequence, one step per token, in float64.
+
+    [Card] "Architecture summary": in the linear (DGA) layers each document is
+    encoded through the layer's recurrence, and the query path runs the
+    chunked gated delta rule starting from an injected initial state.  The
+    pages name the rule but not its equations; the reading here is the
+    published gated delta rule (decay gate alpha = exp(g), writing strength
+    beta), with the state h[k_dim, v_dim] of each (sequence, head):
+
+        h   <- alpha_t * h                       (decay)
+        u    = h^T k_t                           (what the memory predicts for k_t)
+        h   <- h + k_t (beta_t (v_t - u))^T      (delta-rule write)
+        o_t  = scale * h^T q_t
+
+    q, k [B, T, H, dk]; v [B, T, H, dv]; g, beta [B, T, H]; initial_state
+    [B, H, dk, dv] or None (zeros).  scale defaults to 1/sqrt(dk).  Keys are
+    used as given (the caller normalises them if the model does).
+    Returns (o float64 [B, T, H, dv], final state float64 [B, H, dk, dv]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    b_, t_, h_, dk = q.shape
+    dv = v.shape[-1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(dk)
+    h = np.zeros((b_, h_, dk, dv)) if initial_state is None else np.array(initial_state, dtype=np.float64)
+    o = np.empty((b_, t_, h_, dv))
+    for t in range(t_):
+        alpha = np.exp(g[:, t])[:, :, None, None]                     # [B, H, 1, 1]
+        h = alpha * h
+        kt = k[:, t]                                                  # [B, H, dk]
+        u = np.einsum("bhkv,bhk->bhv", h, kt)
+        delta = beta[:, t][:, :, None] * (v[:, t] - u)                # [B, H, dv]
+        h = h + kt[:, :, :, None] * delta[:, :, None, :]
+        o[:, t] = scale * np.einsum("bhkv,bhk->bhv", h, q[:, t])
+    return o, h
+
+
+def inject_states(doc_states, ids):
+    """Initial state of the query path: the sum of the selected documents'
+    states, S_ext[b, h] = sum_i doc_states[ids[b, i], h]  ([Card]
+    "Architecture summary": the top-k documents' recurrent states are summed
+    into S_ext).  doc_states [N_doc, H, dk, dv]; ids [B, k] in [0, N_doc).
+    """
+    s = np.asarray(doc_states, dtype=np.float64)
+    ids = np.asarray(ids)
+    if ids.size and (ids.min() < 0 or ids.max() >= s.shape[0]):
+        raise IndexError("document id out of range")
+    return s[ids].sum(axis=1)
