@@ -1,6 +1,6 @@
 """Benchmark of the MSA routed-layer hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode|interleave|backward|encode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode|interleave|backward|linear|encode]
                     [--no-cpu-baseline]
 
 A step is one pass of the whole hot path over one batch of synthetic input
@@ -21,6 +21,10 @@ already resident in HBM:
            shapes: 2048 tokens, 128 gathered memory rows, 2048 local rows,
            32/8 heads): attention forward -> attention backward (dq; dk, dv of
            the memory and local rows)
+  linear  (the linear-layer variant on the 1M-token bank: 32 sequences x 1
+           token, top-16, 8 heads x 128): route -> top-k -> sum of the
+           selected documents' states -> one gated-delta step from that state
+           (the 2048 document states are encoded beforehand, timed apart)
   encode  (offline encoder: 2048 documents of 256..768 tokens, ~1M tokens,
            8 KV heads x 128, bf16): chunk offsets -> encode K (document-wise
            RoPE, base 1e6) -> encode V -> encode K_r (+ norms)
@@ -66,7 +70,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", choices=["prefill", "decode", "interleave", "backward", "encode"], default="prefill")
+    p.add_argument("--workload", choices=["prefill", "decode", "interleave", "backward", "linear", "encode"], default="prefill")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     # profiling helpers (see "Profiles" in the module docstring)
@@ -160,6 +164,8 @@ STAGE_KERNELS = {
                    "attn": ("attn_prefill", "attn_prefill.hip")},
     "backward": {"attn": ("attn_prefill", "attn_prefill.hip"), "attn_bwd": ("attn_bwd", "attn_backward.hip")},
     # (the backward stage is two kernels, dq then dk/dv; its entry covers both)
+    "linear": {"route": ("route_", "route.hip"), "topk": ("topk", "topk.hip"),
+               "state_sum": ("gdn_state_sum", "gdn.hip"), "gdn": ("gdn_kernel", "gdn.hip")},
     "encode": {"offsets": ("chunk_offsets", "encode.hip"), "encode": ("encode_kernel", "encode.hip")},
     # (both encode launches share one kernel template; the traffic entry covers their average)
 }
@@ -535,6 +541,149 @@ class BackwardStep:
                 "seconds_per_step": secs}
 
 
+class LinearStep:
+    """Linear-layer variant on the 1M-token bank (decode shape): the router
+    bank and queries follow decode-1M-bf16; each document's state comes from
+    the gated delta rule over its 512 tokens (K unit-norm, V N(0,1)/sqrt(128),
+    log-decay -U(0, 0.1), beta U(0, 1)), encoded once before timing; the query
+    token's q, k, v, gates are drawn the same way."""
+
+    def __init__(self, seed, dev):
+        import torch
+        import msa_inputs as mi
+        import routed_sparse_attention_msa_amd as msa
+        self.torch, self.msa, self.cfg = torch, msa, mi.DECODE
+        c = self.cfg
+        base = mi.draw_layer(mi.PREFILL, seed=seed, device=dev)
+        t = mi.draw_layer(c, seed=seed + 1, device=dev, with_raw=False)
+        self.kbar_r = torch.empty((c.n_chunks, c.heads_kv, c.dim), dtype=torch.bfloat16, device=dev)
+        self.knorm = torch.empty((c.n_chunks, c.heads_kv), dtype=torch.float32, device=dev)
+        msa.msa_pool_chunks(base["k_r"], c.chunk, xbar=self.kbar_r, xbar_norm=self.knorm)
+        self.q_r = t["q_r"]
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(seed + 5)
+        h, d = c.heads_kv, c.dim
+
+        def seq(n, t_len):
+            k = torch.randn((n, t_len, h, d), generator=gen, device=dev)
+            k = (k / torch.linalg.vector_norm(k, dim=-1, keepdim=True)).to(torch.bfloat16)
+            v = (torch.randn((n, t_len, h, d), generator=gen, device=dev) / math.sqrt(d)).to(torch.bfloat16)
+            g = -0.1 * torch.rand((n, t_len, h), generator=gen, device=dev)
+            b = torch.rand((n, t_len, h), generator=gen, device=dev)
+            return k, v, g, b
+
+        # offline: every document's state (outputs not needed)
+        dk_, dv_, dg, db = seq(c.n_doc, c.doc_len)
+        self.doc_states = torch.empty((c.n_doc, h, d, d), dtype=torch.float32, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        msa.msa_gated_delta_rule(None, dk_, dv_, dg, db, final_state=self.doc_states, with_out=False)
+        e1.record()
+        torch.cuda.synchronize()
+        self.encode_ms = e0.elapsed_time(e1)
+        del dk_, dv_, dg, db
+        self.k, self.v, self.g, self.beta = seq(c.batch, c.q_len)
+        self.q = (torch.randn((c.batch, c.q_len, h, d), generator=gen, device=dev) / math.sqrt(d)).to(torch.bfloat16)
+        self.scores = torch.empty((c.batch, c.n_doc), dtype=torch.float32, device=dev)
+        self.ids = torch.empty((c.batch, c.topk), dtype=torch.int32, device=dev)
+        self.s_ext = torch.empty((c.batch, h, d, d), dtype=torch.float32, device=dev)
+        self.out = torch.empty((c.batch, c.q_len, h, d), dtype=torch.bfloat16, device=dev)
+        self.final = torch.empty_like(self.s_ext)
+        u8 = lambda n: torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+        self.ws_route = u8(msa.msa_route_scores_workspace(c.batch, c.q_len, h, d, c.n_doc, c.chunks_per_doc,
+                                                          torch.bfloat16))
+        self.ws_topk = u8(msa.msa_topk_docs_workspace(c.batch, c.n_doc, c.topk))
+        torch.cuda.synchronize()
+
+    def calls(self):
+        msa, c = self.msa, self.cfg
+        return [("route", lambda: msa.msa_route_scores(self.q_r, self.kbar_r, self.knorm, c.chunks_per_doc,
+                                                       doc_scores=self.scores, ws=self.ws_route)),
+                ("topk", lambda: msa.msa_topk_docs(self.scores, c.topk, topk_ids=self.ids, with_scores=False,
+                                                   ws=self.ws_topk)),
+                ("state_sum", lambda: msa.msa_gdn_state_sum(self.doc_states, self.ids, s_ext=self.s_ext)),
+                ("gdn", lambda: msa.msa_gated_delta_rule(self.q, self.k, self.v, self.g, self.beta,
+                                                         initial_state=self.s_ext, out=self.out,
+                                                         final_state=self.final))]
+
+    run = Step.run
+
+    def work(self, stage):
+        c = self.cfg
+        st = c.heads_kv * c.dim * c.dim * 4
+        if stage == "route":
+            return work_route(c)
+        if stage == "topk":
+            return work_topk(c)
+        if stage == "state_sum":
+            return {"bound": "hbm", "bytes": c.batch * (c.topk + 1) * st + c.batch * c.topk * 4, "flops": 0}
+        # one step per sequence: the state read and written, q/k/v/out
+        b = 2 * c.batch * st + 4 * c.batch * c.q_len * c.heads_kv * c.dim * 2
+        return {"bound": "hbm", "bytes": b, "flops": 6 * c.batch * c.q_len * c.heads_kv * c.dim * c.dim}
+
+    def cpu_baseline(self):
+        import numpy as np
+        from oracle import gated_delta_rule, inject_states, route_scores, topk_docs
+        try:
+            from threadpoolctl import threadpool_info
+            blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:  # pragma: no cover
+            blas = 1
+        c = self.cfg
+        f = lambda x: x.detach().float().cpu().double().numpy()
+        # the whole step (the selected documents' states copied to the host first, untimed)
+        q_r, kb = f(self.q_r), f(self.kbar_r)
+        t0 = time.perf_counter()
+        sc = route_scores(q_r, kb, c.chunks_per_doc)
+        ids, _ = topk_docs(sc, c.topk)
+        secs = time.perf_counter() - t0
+        st = f(self.doc_states[self.ids.flatten().long()])
+        t0 = time.perf_counter()
+        s_ext = inject_states(st, np.arange(c.batch * c.topk).reshape(c.batch, c.topk))
+        gated_delta_rule(f(self.q), f(self.k), f(self.v), f(self.g), f(self.beta), initial_state=s_ext)
+        secs += time.perf_counter() - t0
+        return {"value": c.batch * c.q_len / secs, "unit": "query tokens/s", "cores": int(blas), "kind": "oracle",
+                "sample": "the whole step (route over all documents, top-k, state sum and the step for all "
+                          f"{c.batch} sequences)", "seconds_per_step": secs}
+
+
+def main_linear(args):
+    import torch
+    print("[bench] building inputs for linear-1M-decode-bf16 (encoding 2048 document states)", file=sys.stderr,
+          flush=True)
+    step = LinearStep(args.seed, "cuda:0")
+    step.run(args.warmup, events=False)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    marks = step.run(args.steps, events=True)
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    stages = stage_summary(step, marks, args.steps)
+    dom = max(stages, key=lambda k: stages[k]["ms_per_step"])
+    roof = {k: stages[dom][k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+    roof.update({"kernel": dom, "avg_launch_ms": stages[dom]["avg_launch_ms"],
+                 "traffic": measured_traffic("linear", dom)})
+    c = step.cfg
+    rec = {
+        "metric": "query tokens/s of the linear-layer variant at 1M-token memory (decode step)",
+        "value": c.batch * c.q_len / (ms_per_step / 1e3), "unit": "query tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "linear-1M-decode-bf16", "n_docs": c.n_doc, "doc_len": c.doc_len, "batch": c.batch,
+                   "q_len": c.q_len, "heads": c.heads_kv, "dk": c.dim, "dv": c.dim, "topk": c.topk,
+                   "step": "route -> top-k -> state sum -> gated-delta step",
+                   "offline_document_states_ms": step.encode_ms},
+        "roofline": roof, "stages": stages,
+        "cpu_baseline": None if args.no_cpu_baseline else step.cpu_baseline(),
+    }
+    print(json.dumps(rec))
+
+
 def main_backward(args):
     import torch
     dev = "cuda:0"
@@ -731,6 +880,9 @@ def main():
         return
     if args.workload == "backward":
         main_backward(args)
+        return
+    if args.workload == "linear":
+        main_linear(args)
         return
     import torch
     import msa_inputs as mi

@@ -292,6 +292,38 @@ msa_status msa_sparse_attn_backward(const void* q, const void* k_sel, const void
                                     msa_dtype dt, void* d_q, void* d_k_sel, void* d_v_sel, void* d_k_loc,
                                     void* d_v_loc, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Linear-layer variant (model card "Architecture summary": in the linear
+ *     gated-delta layers each document is encoded through the layer's
+ *     recurrence, the routed top-k documents' recurrent states are summed
+ *     into S_ext, and the query path runs the gated delta rule with S_ext as
+ *     its initial state).  Routing is msa_route_scores / msa_topk_docs.
+ *
+ * msa_gdn_state_sum: s_ext[b] = sum_{i<k} doc_states[topk_ids[b,i]], in rank
+ *   order.  doc_states [n_docs, heads, dk, dv] float32; s_ext [batch, heads,
+ *   dk, dv] float32; ids outside [0, n_docs) contribute nothing.
+ *
+ * msa_gated_delta_rule: per (sequence b, head h), state S[dk][dv] starting at
+ *   initial_state[b,h] (or zeros when NULL), for each token t in order:
+ *       S <- exp(g[b,t,h]) * S
+ *       u  = S^T k[b,t,h]
+ *       S <- S + k[b,t,h] (beta[b,t,h] * (v[b,t,h] - u))^T
+ *       out[b,t,h] = scale * S^T q[b,t,h]
+ *   (the published gated delta rule; the pages name it without equations).
+ *   q, k [batch, seq_len, heads, dk]; v, out [batch, seq_len, heads, dv]
+ *   (dtype dt); g (log decay), beta [batch, seq_len, heads] float32;
+ *   initial_state, final_state [batch, heads, dk, dv] float32.  out or
+ *   final_state may be NULL (not both); q may be NULL when out is NULL (the
+ *   offline document encoding: final states only).  dk is 64 or 128.
+ *   Keys are used as given (normalise them first if the model does).
+ * ---------------------------------------------------------------------- */
+msa_status msa_gdn_state_sum(const float* doc_states, const int32_t* topk_ids, int32_t batch, int32_t k,
+                             int64_t n_docs, int32_t heads, int32_t dk, int32_t dv, float* s_ext, void* stream);
+msa_status msa_gated_delta_rule(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                float scale, const float* initial_state, int32_t batch, int32_t seq_len,
+                                int32_t heads, int32_t dk, int32_t dv, msa_dtype dt, void* out,
+                                float* final_state, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

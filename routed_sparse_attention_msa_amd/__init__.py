@@ -13,6 +13,8 @@ of ``include/msa.h``; this package is its thin Python binding:
     msa_gather_kv            S4  gather (or host-tier fetch) of the selected pooled K/V
     msa_sparse_attn          S5/S6 sparse GQA attention (prefill and decode)
     msa_sparse_attn_backward its gradients (training through the routed layer)
+    msa_gdn_state_sum        linear-layer variant: sum of the selected documents' states
+    msa_gated_delta_rule       and the gated delta rule from that initial state
 """
 
 from ._lib import (  # noqa: F401
@@ -21,7 +23,9 @@ from ._lib import (  # noqa: F401
     lib,
     msa_chunk_offsets,
     msa_encode_docs,
+    msa_gated_delta_rule,
     msa_gather_kv,
+    msa_gdn_state_sum,
     msa_pool_chunks,
     msa_route_rounds,
     msa_route_rounds_workspace,

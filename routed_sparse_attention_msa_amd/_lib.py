@@ -59,6 +59,10 @@ SIGNATURES = {
                                            c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
                                            c_int32, c_float, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                                            c_void_p, c_void_p, c_size_t, c_void_p]),
+    "msa_gdn_state_sum": (_STATUS, [c_void_p, c_void_p, c_int32, c_int32, c_int64, c_int32, c_int32, c_int32,
+                                    c_void_p, c_void_p]),
+    "msa_gated_delta_rule": (_STATUS, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_int32,
+                                       c_int32, c_int32, c_int32, c_int32, c_int, c_void_p, c_void_p, c_void_p]),
 }
 
 
@@ -489,3 +493,66 @@ def msa_sparse_attn_backward(q, k_sel, v_sel, k_loc, v_loc, out, lse, d_out, sca
                                           _ptr(d_vs), _ptr(d_kl), _ptr(d_vl), _ptr(ws), ws_bytes,
                                           _stream(q.device)))
     return d_q, d_ks, d_vs, d_kl, d_vl
+
+
+# ---------------------------------------------------------------------------
+# Linear-layer variant
+# ---------------------------------------------------------------------------
+
+def msa_gdn_state_sum(doc_states, topk_ids, s_ext=None):
+    """S_ext [batch, heads, dk, dv] = sum of ``doc_states`` [n_docs, heads, dk, dv] (float32) over the
+    documents in ``topk_ids`` [batch, k] (int32), in rank order."""
+    _dev(doc_states, "doc_states", dtype=torch.float32, ndim=4)
+    _dev(topk_ids, "topk_ids", dtype=torch.int32, ndim=2)
+    n_docs, heads, dk, dv = doc_states.shape
+    batch, k = topk_ids.shape
+    if s_ext is None:
+        s_ext = torch.empty((batch, heads, dk, dv), dtype=torch.float32, device=doc_states.device)
+    _dev(s_ext, "s_ext", dtype=torch.float32)
+    if s_ext.shape != (batch, heads, dk, dv):
+        raise ValueError("s_ext must be [batch, heads, dk, dv]")
+    _check(lib().msa_gdn_state_sum(_ptr(doc_states), _ptr(topk_ids), batch, k, n_docs, heads, dk, dv, _ptr(s_ext),
+                                   _stream(doc_states.device)))
+    return s_ext
+
+
+def msa_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None, out=None, final_state=None,
+                         with_out=True, with_final_state=True):
+    """Gated delta rule over each sequence: q, k [batch, T, heads, dk]; v [batch, T, heads, dv];
+    g (log decay), beta [batch, T, heads] float32; initial_state [batch, heads, dk, dv] float32 or None.
+    Returns (out [batch, T, heads, dv] or None, final_state [batch, heads, dk, dv] float32 or None).
+    ``q`` may be None when ``with_out`` is False (document encoding: final states only)."""
+    _dev(k, "k", ndim=4)
+    _dev(v, "v", dtype=k.dtype, ndim=4)
+    _dev(g, "g", dtype=torch.float32, ndim=3)
+    _dev(beta, "beta", dtype=torch.float32, ndim=3)
+    batch, seq_len, heads, dk = k.shape
+    dv = v.shape[-1]
+    if v.shape[:3] != (batch, seq_len, heads) or g.shape != (batch, seq_len, heads) or beta.shape != g.shape:
+        raise ValueError("k, v, g and beta disagree in shape")
+    if with_out:
+        _dev(q, "q", dtype=k.dtype, ndim=4)
+        if q.shape != k.shape:
+            raise ValueError("q and k must have the same shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    if initial_state is not None:
+        _dev(initial_state, "initial_state", dtype=torch.float32)
+        if initial_state.shape != (batch, heads, dk, dv):
+            raise ValueError("initial_state must be [batch, heads, dk, dv]")
+    if with_out and out is None:
+        out = torch.empty((batch, seq_len, heads, dv), dtype=k.dtype, device=k.device)
+    if out is not None:
+        _dev(out, "out", dtype=k.dtype)
+        if out.shape != (batch, seq_len, heads, dv):
+            raise ValueError("out must be [batch, T, heads, dv]")
+    if with_final_state and final_state is None:
+        final_state = torch.empty((batch, heads, dk, dv), dtype=torch.float32, device=k.device)
+    if final_state is not None:
+        _dev(final_state, "final_state", dtype=torch.float32)
+        if final_state.shape != (batch, heads, dk, dv):
+            raise ValueError("final_state must be [batch, heads, dk, dv]")
+    _check(lib().msa_gated_delta_rule(_ptr(q) if with_out else None, _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      float(scale), _ptr(initial_state), batch, seq_len, heads, dk, dv,
+                                      _dtype_code(k), _ptr(out), _ptr(final_state), _stream(k.device)))
+    return out, final_state

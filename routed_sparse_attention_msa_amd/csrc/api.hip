@@ -508,4 +508,36 @@ msa_status msa_sparse_attn_backward(const void* q, const void* k_sel, const void
                     "msa_sparse_attn_backward launch");
 }
 
+// ---------------------------------------------------------------------------
+// Linear-layer variant
+msa_status msa_gdn_state_sum(const float* doc_states, const int32_t* topk_ids, int32_t batch, int32_t k,
+                             int64_t n_docs, int32_t heads, int32_t dk, int32_t dv, float* s_ext, void* stream) {
+  CHECK_ARG(batch > 0 && k > 0 && n_docs > 0 && heads > 0 && dk > 0 && dv > 0, "sizes must be positive");
+  CHECK_ARG(batch <= 65535, "batch above 65535 is not supported");
+  CHECK_ARG(((int64_t)heads * dk * dv) % 4 == 0, "heads*dk*dv must be a multiple of 4");
+  CHECK_ARG(doc_states && topk_ids && s_ext, "null tensor pointer");
+  CHECK_ARG(aligned16(doc_states) && aligned16(s_ext) && ((uintptr_t)topk_ids & 3u) == 0,
+            "tensors must be 16-byte aligned");
+  return hip_status(msa::launch_gdn_state_sum(doc_states, topk_ids, batch, k, n_docs, (int64_t)heads * dk * dv,
+                                              s_ext, static_cast<hipStream_t>(stream)),
+                    "msa_gdn_state_sum launch");
+}
+
+msa_status msa_gated_delta_rule(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                float scale, const float* initial_state, int32_t batch, int32_t seq_len,
+                                int32_t heads, int32_t dk, int32_t dv, msa_dtype dt, void* out,
+                                float* final_state, void* stream) {
+  CHECK_ARG(valid_dtype(dt), "unknown dtype %d", (int)dt);
+  CHECK_ARG(batch > 0 && seq_len >= 0 && heads > 0 && dv > 0, "sizes must be positive");
+  CHECK_ARG(dk == 64 || dk == 128, "dk must be 64 or 128 (got %d)", dk);
+  CHECK_ARG(batch <= 65535 && heads <= 65535, "batch and heads must be at most 65535");
+  CHECK_ARG(out != nullptr || final_state != nullptr, "nothing to compute: out and final_state are both NULL");
+  CHECK_ARG(scale == scale, "scale is NaN");
+  CHECK_ARG(seq_len == 0 || (k && v && g && beta && (out == nullptr || q)), "null tensor pointer");
+  if (seq_len == 0 && final_state == nullptr) return MSA_OK;
+  return hip_status(msa::launch_gdn(q, k, v, g, beta, scale, initial_state, batch, seq_len, heads, dk, dv, dt, out,
+                                    final_state, static_cast<hipStream_t>(stream)),
+                    "msa_gated_delta_rule launch");
+}
+
 }  // extern "C"

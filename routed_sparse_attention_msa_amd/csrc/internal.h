@@ -140,4 +140,10 @@ hipError_t launch_attn_backward(const void* q, const void* k_sel, const void* v_
                                 int heads_kv, int dim, float scale, msa_dtype dt, void* dq, void* dk_sel,
                                 void* dv_sel, void* dk_loc, void* dv_loc, void* ws, hipStream_t s);
 
+hipError_t launch_gdn_state_sum(const float* states, const int32_t* ids, int batch, int k, int64_t n_docs,
+                                int64_t per_doc, float* out, hipStream_t s);
+hipError_t launch_gdn(const void* q, const void* k, const void* v, const float* g, const float* beta, float scale,
+                      const float* init, int batch, int seq_len, int heads, int dk, int dv, msa_dtype dt,
+                      void* out, float* final_state, hipStream_t s);
+
 }  // namespace msa
