@@ -55,6 +55,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -147,30 +148,45 @@ def roofline_entry(work, ms):
 # measured HBM traffic (rocprofv3 counters), valid only for the source it was taken on
 # ---------------------------------------------------------------------------
 
-def kernel_source_sha(src_file):
-    path = os.path.join(ROOT, "routed_sparse_attention_msa_amd", "csrc", src_file)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_sha(src_files):
+    """Hash of kernel sources (names separated by |) and of the local headers they include."""
+    csrc = os.path.join(ROOT, "routed_sparse_attention_msa_amd", "csrc")
+    h = hashlib.sha256()
+    todo, seen = src_files.split("|"), set()
+    while todo:
+        name = todo.pop(0)
+        path = os.path.normpath(os.path.join(csrc, name))
+        if path in seen or not os.path.exists(path):
+            continue
+        seen.add(path)
+        with open(path, "rb") as f:
+            data = f.read()
+        h.update(data)
+        todo += re.findall(r'#include "([^"]+)"', data.decode("utf-8", "replace"))
+    return h.hexdigest()[:16]
 
 
-# stage -> (kernel-name pattern, source file), per workload
+INTERLEAVE_ROUNDS = 3
+
+# stage -> (kernel-name patterns separated by |, source file[, launches of each kernel per stage call])
 STAGE_KERNELS = {
     "prefill": {"pool": ("pool_kernel", "pool.hip"), "route": ("route_", "route.hip"),
                 "topk": ("topk", "topk.hip"), "gather": ("gather", "gather.hip"),
                 "attn": ("attn_prefill", "attn_prefill.hip")},
     "decode": {"route": ("route_", "route.hip"), "topk": ("topk", "topk.hip"),
                "gather": ("gather", "gather.hip"), "attn": ("attn_decode", "attn_decode.hip")},
-    "interleave": {"rounds": ("route_", "route.hip"), "gather": ("gather", "gather.hip"),
+    "interleave": {"rounds": ("route_|topk", "route.hip|topk.hip", INTERLEAVE_ROUNDS), "gather": ("gather", "gather.hip"),
                    "attn": ("attn_prefill", "attn_prefill.hip")},
     "backward": {"attn": ("attn_prefill", "attn_prefill.hip"), "attn_bwd": ("attn_bwd", "attn_backward.hip")},
     # (the backward stage is two kernels, dq then dk/dv; its entry covers both)
     "linear": {"route": ("route_", "route.hip"), "topk": ("topk", "topk.hip"),
-               "state_sum": ("gdn_state_sum", "gdn.hip"), "gdn": ("gdn_kernel", "gdn.hip")},
-    "encode": {"offsets": ("chunk_offsets", "encode.hip"), "encode": ("encode_kernel", "encode.hip")},
-    # (both encode launches share one kernel template; the traffic entry covers their average)
+               "state_sum": ("gdn_state_sum", "gdn.hip"), "gdn": ("gdn_kernel<unsigned short, 128, true>", "gdn.hip")},
+    "encode": {"offsets": ("chunk_offsets", "encode.hip"),
+               "encode_rope": ("encode_kernel<unsigned short, true>", "encode.hip"),
+               "encode": ("encode_kernel<unsigned short, false>", "encode.hip")},
+    # (the two plain encode launches share one kernel; its entry is their median)
 }
 COPY_PROBE_BYTES = 1 << 30
-INTERLEAVE_ROUNDS = 3
 
 
 def measured_traffic(workload, stage):
@@ -243,19 +259,21 @@ def summarize_traffic(d):
         if not fm or not wm:
             continue
         out[wl] = {}
-        for stage, (pat, src) in stages.items():
-            names = sorted(k for k in fm if pat in k and "msa::" in k)
+        for stage, spec in stages.items():
+            pat, src = spec[0], spec[1]
+            per_call = spec[2] if len(spec) > 2 else 1          # launches of each kernel per stage call
+            names = sorted(k for k in fm if "msa::" in k and any(p in k for p in pat.split("|")))
             if not names:
                 continue
-            rd = sum(fm[k] for k in names) * 1024 * fetch_factor
-            wr = sum(wm.get(k, 0.0) for k in names) * 1024 * write_factor
+            rd = per_call * sum(fm[k] for k in names) * 1024 * fetch_factor
+            wr = per_call * sum(wm.get(k, 0.0) for k in names) * 1024 * write_factor
             out[wl][stage] = {"source_sha": kernel_source_sha(src), "read_bytes": rd, "write_bytes": wr,
                               "bytes_per_launch": rd + wr, "kernels": names}
             short = ", ".join(sorted({_short_kernel(n) for n in names}))
             md.append(f"| {wl} | {stage} | `{short}` | {rd / 1e6:.1f} | {wr / 1e6:.1f} | {(rd + wr) / 1e6:.1f} |")
     with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
         json.dump(out, f, indent=1)
-    with open(os.path.join(ROOT, "profiles", "hbm-traffic_prefill-and-decode-steps.md"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", "hbm-traffic_per-stage_all-workloads.md"), "w") as f:
         f.write("\n".join(md) + "\n")
     print(json.dumps(out, indent=1))
 
