@@ -28,7 +28,10 @@
 // softmax scale is folded into one FMA before exp2, and probabilities are
 // packed to bf16 by the hardware converter.
 //
-// Work split: one workgroup = (sequence, KV head, 32-token block).  Its waves
+// Work split: one workgroup = (sequence, KV head, a pair of 32-token blocks
+// taken one after the other: the block with the longest causal rows and its
+// mirror with the shortest, so every workgroup has about the same number of
+// key tiles).  Its waves
 // are the query heads of that KV group (GQA packing: each K/V tile is staged
 // once for all of them) times two key halves: one wave set takes the even
 // 64-key tiles, the other the odd ones, each with its own double-buffered
@@ -38,7 +41,6 @@
 // every key.  Key tiles cover the memory rows, then the local rows (a tile
 // never mixes the two); tiles fully below every query's causal limit skip
 // the mask, tiles beyond the last query's limit are never loaded.
-// Workgroups are issued longest-first.
 #include "attn_common.h"
 
 namespace msa {
@@ -380,9 +382,9 @@ hipError_t launch_attn_prefill(const void* q, const void* k_sel, const void* v_s
     return e;
   }();
   if (attr != hipSuccess) return attr;
-  // Split each workgroup's keys over two wave sets when the grid is a single
-  // round of workgroups (the longest block then bounds the kernel); with many
-  // rounds the longest-first order balances the CUs on its own.
+  // Split each workgroup's keys over two wave sets when the grid is at most
+  // one round of workgroups (each then runs on a CU of its own); with more
+  // rounds, two unsplit workgroups share a CU.
   const bool split = (int)grid <= 2 * device_cu_count();
   const float sl2 = scale * kLog2e;
   auto go = [&](auto kern, int threads, size_t smem) {
