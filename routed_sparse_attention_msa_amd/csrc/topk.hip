@@ -204,6 +204,112 @@ __global__ __launch_bounds__(kThreads) void topk_tile_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Rows of at most one tile with k <= 64 (the routing and decode sizes): each
+// lane sorts its few keys in registers, each wave takes out its k largest by
+// repeated wave maxima (DPP reductions, the result broadcast through a
+// scalar register), and wave 0 takes the final k out of the four waves'
+// candidates.  One barrier instead of the radix passes' dozens; exact like
+// them (the keys are unique).
+constexpr int kSmallMaxK = 64;
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  // quad xor 1, quad xor 2, row half-mirror, row mirror: every lane holds its
+  // row's max; row broadcasts 15 and 31 carry the rows' maxima to lane 63
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Largest 64-bit key of the wave (the high words first, then the low words
+// of the lanes that hold the largest high word).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  const uint32_t hi = wave_max_u32((uint32_t)(v >> 32));
+  const uint32_t lo = wave_max_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Descending bitonic sort of a register array (constant indices throughout).
+template <int N>
+__device__ __forceinline__ void sort_desc(uint64_t (&a)[N]) {
+#pragma unroll
+  for (int size = 2; size <= N; size <<= 1)
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool desc = (i & size) == 0;
+          const uint64_t x = a[i], y = a[j];
+          const bool swap = desc ? x < y : x > y;
+          a[i] = swap ? y : x;
+          a[j] = swap ? x : y;
+        }
+      }
+}
+
+// Take the k largest keys out of the wave's sorted per-lane lists; lane r
+// receives the r-th largest (0 once the wave runs out).
+template <int N>
+__device__ __forceinline__ uint64_t wave_extract(uint64_t (&a)[N], int k, int lane) {
+  uint64_t mine = 0;
+  for (int r = 0; r < k; ++r) {
+    const uint64_t m = wave_max_u64(a[0]);
+    if (m == 0) break;                           // uniform: every lane sees the same maximum
+    if (lane == r) mine = m;
+    const bool pop = a[0] == m;                  // exactly one lane: the keys are unique
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j) a[j] = pop ? a[j + 1] : a[j];
+    a[N - 1] = pop ? 0 : a[N - 1];
+  }
+  return mine;
+}
+
+template <int ITEMS>
+__global__ __launch_bounds__(kThreads) void topk_small_kernel(
+    const float* __restrict__ scores, int64_t n, int k, const int32_t* excl, int n_excl, int64_t excl_stride,
+    int32_t* ids_out, float* vals_out, int64_t out_stride) {
+  __shared__ uint32_t excl_bits[kTile / 32];
+  __shared__ uint64_t cand[kThreads / 64][kSmallMaxK];
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (n_excl > 0) {
+    for (int i = tid; i < kTile / 32; i += kThreads) excl_bits[i] = 0;
+    __syncthreads();
+    for (int j = tid; j < n_excl; j += kThreads) {
+      const int64_t id = excl[(size_t)b * excl_stride + j];
+      if (id >= 0 && id < n) atomicOr(&excl_bits[id >> 5], 1u << (id & 31));
+    }
+    __syncthreads();
+  }
+  uint64_t a[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int idx = i * kThreads + tid;
+    const bool ok = idx < n && !(n_excl > 0 && ((excl_bits[idx >> 5] >> (idx & 31)) & 1u));
+    a[i] = ok ? make_key(scores[(size_t)b * n + idx], (uint32_t)idx) : 0;
+  }
+  sort_desc(a);
+  const uint64_t mine = wave_extract(a, k, lane);
+  if (lane < k) cand[wave][lane] = mine;
+  __syncthreads();
+  if (wave != 0) return;
+  uint64_t c[kThreads / 64];
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) c[w] = lane < k ? cand[w][lane] : 0;
+  sort_desc(c);
+  const uint64_t best = wave_extract(c, k, lane);
+  if (lane < k) {
+    ids_out[(size_t)b * out_stride + lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)best);
+    if (vals_out) vals_out[(size_t)b * out_stride + lane] = unorder_score((uint32_t)(best >> 32));
+  }
+}
+
 inline int next_pow2(int v) {
   int p = 1;
   while (p < v) p <<= 1;
@@ -228,6 +334,15 @@ hipError_t launch_topk_excl(const float* scores, int batch, int64_t n_docs, int 
                             int64_t out_stride, void* ws, hipStream_t s) {
   const int kp2 = next_pow2(k);
   int64_t tiles = (n_docs + kTile - 1) / kTile;
+  if (tiles <= 1 && k <= kSmallMaxK) {
+    if (n_docs <= kTile / 2)
+      hipLaunchKernelGGL(topk_small_kernel<kItems / 2>, dim3(1, batch), dim3(kThreads), 0, s, scores, n_docs, k,
+                         excl, n_excl, excl_stride, ids, vals, out_stride);
+    else
+      hipLaunchKernelGGL(topk_small_kernel<kItems>, dim3(1, batch), dim3(kThreads), 0, s, scores, n_docs, k, excl,
+                         n_excl, excl_stride, ids, vals, out_stride);
+    return hipGetLastError();
+  }
   if (tiles <= 1) {
     hipLaunchKernelGGL((topk_tile_kernel<false, true>), dim3(1, batch), dim3(kThreads), 0, s,
                        scores, nullptr, n_docs, k, kp2, excl, n_excl, excl_stride, nullptr, ids, vals,
