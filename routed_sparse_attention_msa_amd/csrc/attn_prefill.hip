@@ -57,7 +57,7 @@ struct PrefillSmem {
 };
 
 template <int NW, int SPLIT>
-__global__ __launch_bounds__(NW * 64 * SPLIT, SPLIT == 1 && NW == 4 ? 2 : 1) void attn_prefill_kernel(
+__global__ __launch_bounds__(NW * 64 * SPLIT) void attn_prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_sel,
     const uint16_t* __restrict__ v_sel, int mem_len, const uint16_t* __restrict__ k_loc,
     const uint16_t* __restrict__ v_loc, int loc_len, int batch, int q_len, int heads_q, int heads_kv,
@@ -351,9 +351,11 @@ __global__ __launch_bounds__(NW * 64 * SPLIT, SPLIT == 1 && NW == 4 ? 2 : 1) voi
 
 
 // ---------------------------------------------------------------------------
-// Ping-pong variant (groups of 4 query heads per KV head, one round of
-// workgroups).  Same work split, orientation and online softmax as above; what
-// changes is how the two key halves share a SIMD and how tiles reach LDS.
+// Ping-pong variant, for groups of 4 query heads per KV head (the GQA shapes
+// of the routed layers; the kernel above serves groups of 1 and 2).  Same
+// work split, orientation and online softmax as above, always with two key
+// halves; what changes is how the two halves share a SIMD and how tiles reach
+// LDS.
 //
 // The waves of the two key halves that share a SIMD (the same query head) run
 // half a step apart: the workgroup's barriers cut time into slots, and in each
@@ -776,19 +778,19 @@ hipError_t launch_attn_prefill(const void* q, const void* k_sel, const void* v_s
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     };
-    set(attn_prefill_kernel<4, 1>, sizeof(PrefillSmem));
     set(attn_prefill_kernel<2, 1>, sizeof(PrefillSmem));
     set(attn_prefill_kernel<1, 1>, sizeof(PrefillSmem));
-    set(attn_prefill_kernel<4, 2>, 2 * sizeof(PrefillSmem));
     set(attn_prefill_kernel<2, 2>, 2 * sizeof(PrefillSmem));
     set(attn_prefill_kernel<1, 2>, 2 * sizeof(PrefillSmem));
     set(attn_prefill_pp_kernel, 2 * sizeof(PingPongSmem));
     return e;
   }();
   if (attr != hipSuccess) return attr;
-  // Split each workgroup's keys over two wave sets when the grid is at most
-  // one round of workgroups (each then runs on a CU of its own); with more
-  // rounds, two unsplit workgroups share a CU.
+  // Groups of 4 query heads: the ping-pong kernel (one workgroup per CU, its
+  // keys split over two wave sets), whatever the grid.  Groups of 1 or 2:
+  // split the keys when the grid is at most one round of workgroups (each
+  // then runs on a CU of its own); with more rounds, two unsplit workgroups
+  // share a CU.
   const bool split = (int)grid <= 2 * device_cu_count();
   const float sl2 = scale * kLog2e;
   auto go = [&](auto kern, int threads, size_t smem) {
@@ -800,12 +802,11 @@ hipError_t launch_attn_prefill(const void* q, const void* k_sel, const void* v_s
     return hipGetLastError();
   };
   const size_t one = sizeof(PrefillSmem);
+  if (nw == 4) return go(attn_prefill_pp_kernel, 512, 2 * sizeof(PingPongSmem));
   if (split) {
-    if (nw == 4) return go(attn_prefill_pp_kernel, 512, 2 * sizeof(PingPongSmem));
     if (nw == 2) return go(attn_prefill_kernel<2, 2>, 256, 2 * one);
     return go(attn_prefill_kernel<1, 2>, 128, 2 * one);
   }
-  if (nw == 4) return go(attn_prefill_kernel<4, 1>, 256, one);
   if (nw == 2) return go(attn_prefill_kernel<2, 1>, 128, one);
   return go(attn_prefill_kernel<1, 1>, 64, one);
 }
