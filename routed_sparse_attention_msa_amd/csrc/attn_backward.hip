@@ -368,15 +368,19 @@ __global__ __launch_bounds__(NWK * 64) void attn_bwd_dkdv_kernel(
     const uint32_t nbytes = (uint32_t)((size_t)q_len * qrs - (size_t)h * kD * 2);
     const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc((void*)(q + base), (short)0, nbytes, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t orr = __builtin_amdgcn_make_buffer_rsrc((void*)(d_out + base), (short)0, nbytes, kRsrcWord3);
+    // the tile's first row goes in the scalar offset, the lane's row in the
+    // vector offset (a per-lane scalar offset would make the compiler loop
+    // over its distinct values)
+    const uint32_t soff = (uint32_t)tq0 * qrs;
 #pragma unroll
     for (int i = 0; i < kTTasks; ++i) {
       const int c = tid + kThreads * i;
       const int r0 = vtask_row0(c);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t soff = (uint32_t)(tq0 + r0 + j) * qrs;
-        tq[i][j] = bload(qr, (c & 15) * 16, soff);
-        to[i][j] = bload(orr, (c & 15) * 16, soff);
+        const uint32_t voff = (uint32_t)(r0 + j) * qrs + (c & 15) * 16;
+        tq[i][j] = bload(qr, voff, soff);
+        to[i][j] = bload(orr, voff, soff);
       }
     }
     const int tt = tq0 + (tid & (kQT - 1));

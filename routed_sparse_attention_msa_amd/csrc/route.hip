@@ -586,13 +586,20 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
   // Buffer loads: a per-lane offset fixed for the kernel plus the stage's
   // scalar offset; rows past t_tot / n_ch lie beyond the resources' records
   // and read as zeros, so the loads carry no branches and no address math.
+  // (Base and size pass through readfirstlane: the compiler did not prove
+  // them uniform and wrapped every load in a loop over the lanes' values.)
   const uint32_t row_bytes = (uint32_t)(row_elems * 2);
-  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(q_r + (size_t)row0 * row_elems), 0,
-      (int)((size_t)max(0, min(kTB, t_tot - row0)) * row_bytes), 0x00020000);
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(kbar + (size_t)col0 * row_elems), 0,
-      (int)((size_t)max<int64_t>(0, min<int64_t>(kNB, n_ch - col0)) * row_bytes), 0x00020000);
+  auto uniform_rsrc = [](const uint16_t* p, size_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void* u = reinterpret_cast<void*>((uintptr_t)(((uint64_t)hi << 32) | lo));
+    return __builtin_amdgcn_make_buffer_rsrc(u, 0, (int)__builtin_amdgcn_readfirstlane((uint32_t)bytes), 0x00020000);
+  };
+  const __amdgpu_buffer_rsrc_t qrs =
+      uniform_rsrc(q_r + (size_t)row0 * row_elems, (size_t)max(0, min(kTB, t_tot - row0)) * row_bytes);
+  const __amdgpu_buffer_rsrc_t krs =
+      uniform_rsrc(kbar + (size_t)col0 * row_elems, (size_t)max<int64_t>(0, min<int64_t>(kNB, n_ch - col0)) * row_bytes);
   uint32_t voff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
