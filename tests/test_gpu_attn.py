@@ -63,6 +63,8 @@ def _check(q, ks, vs, kl, vl, rtol, lse_atol):
     (32, 1, 32, 8, 128, 32, 250, torch.bfloat16),      # decode, one workgroup per (sequence, KV head)
     (40, 2, 16, 8, 128, 16, 90, torch.bfloat16),       # more pairs than CUs, 2 tokens
     (1, 1, 8, 1, 128, 64, 5000, torch.bfloat16),       # one pair: many runs of splits, combined
+    (1, 96, 8, 2, 128, 64, 160, torch.bfloat16),       # 3 token blocks: a block pair and a middle block alone
+    (1, 80, 16, 2, 128, 40, 100, torch.bfloat16),      # group of 8 heads (two head sub-groups), partial tiles
 ])
 def test_attn_parity(batch, q_len, hq, hkv, dim, mem, loc, dtype):
     case(f"attn B={batch} T={q_len} Hq={hq} Hkv={hkv} d={dim} M={mem} L={loc} {dtype}")
@@ -72,8 +74,8 @@ def test_attn_parity(batch, q_len, hq, hkv, dim, mem, loc, dtype):
 
 
 def test_attn_many_workgroups_sampled():
-    """More workgroups than one round on the GPU (the unsplit prefill kernel);
-    sampled rows against the oracle one by one."""
+    """More workgroups than one round on the GPU (partial memory and local
+    tiles too); sampled rows against the oracle one by one."""
     from oracle import sparse_attention_rows
     case("attn many workgroups (sampled)")
     b_, t_, hq, hkv, d, mem, loc = 3, 1024, 32, 8, 128, 96, 1100
