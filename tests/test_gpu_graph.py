@@ -1,0 +1,90 @@
+"""A routed decode step captured in a HIP graph: every replay reproduces the
+eager step bit for bit (the kernels are deterministic), with eager work and
+synchronisations between the replays, and a replay after the inputs change
+matches an eager step on the new inputs."""
+
+import math
+
+import pytest
+import torch
+
+import routed_sparse_attention_msa_amd as msa
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _inputs(seed):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    n_docs, cpd, heads_kv, heads_q, dim, batch, loc = 256, 8, 4, 16, 128, 8, 700
+    r = lambda *s: (torch.randn(s, generator=g, device=DEV) / math.sqrt(dim)).to(torch.bfloat16)
+    raw_k, raw_v, raw_r = r(n_docs, cpd * 64, heads_kv, dim), r(n_docs, cpd * 64, heads_kv, dim), r(n_docs, cpd * 64, heads_kv, dim)
+    kbar, _ = msa.msa_pool_chunks(raw_k, 64)
+    vbar, _ = msa.msa_pool_chunks(raw_v, 64)
+    kbar_r, knorm = msa.msa_pool_chunks(raw_r, 64, with_norm=True)
+    return dict(kbar=kbar, vbar=vbar, kbar_r=kbar_r, knorm=knorm, cpd=cpd, topk=8,
+                q_r=r(batch, 1, heads_kv, dim), q=r(batch, 1, heads_q, dim) * 4,
+                k_loc=r(batch, loc, heads_kv, dim), v_loc=r(batch, loc, heads_kv, dim))
+
+
+class _Step:
+    def __init__(self, t):
+        self.t = t
+        b = t["q"].shape[0]
+        e = lambda *shape, dt=torch.bfloat16: torch.empty(shape, dtype=dt, device=DEV)
+        self.scores = e(b, t["kbar"].shape[0] // t["cpd"], dt=torch.float32)
+        self.ids = e(b, t["topk"], dt=torch.int32)
+        self.top = e(b, t["topk"], dt=torch.float32)
+        self.k_sel = e(b, t["topk"] * t["cpd"], t["kbar"].shape[1], t["kbar"].shape[2])
+        self.v_sel = torch.empty_like(self.k_sel)
+        self.out = torch.empty_like(t["q"])
+        self.lse = e(b, t["q"].shape[2], 1, dt=torch.float32)
+
+    def __call__(self):
+        t = self.t
+        msa.msa_route_scores(t["q_r"], t["kbar_r"], t["knorm"], t["cpd"], doc_scores=self.scores)
+        msa.msa_topk_docs(self.scores, t["topk"], topk_ids=self.ids, topk_scores=self.top)
+        msa.msa_gather_kv(t["kbar"], t["vbar"], self.ids, t["cpd"], k_sel=self.k_sel, v_sel=self.v_sel)
+        msa.msa_sparse_attn(t["q"], self.k_sel, self.v_sel, t["k_loc"], t["v_loc"], out=self.out, lse=self.lse)
+
+    def results(self):
+        return [x.clone() for x in (self.scores, self.ids, self.top, self.out, self.lse)]
+
+
+def test_graph_replays_match_eager_steps():
+    t = _inputs(5)
+    step = _Step(t)
+    step()
+    torch.cuda.synchronize()
+    want = step.results()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    other = _Step(_inputs(6))
+    for rep in range(4):
+        for x in (step.scores, step.out, step.lse):           # clobber the outputs with a fill kernel
+            x.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        got = step.results()
+        for a, b in zip(got, want):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager step"
+        other()                                              # eager work between replays
+        torch.cuda.synchronize()
+    # new inputs in place: a replay equals an eager step on them
+    t["q_r"].copy_(_inputs(7)["q_r"])
+    t["q"].mul_(0.5)
+    g.replay()
+    torch.cuda.synchronize()
+    got = step.results()
+    step()
+    torch.cuda.synchronize()
+    for a, b in zip(got, step.results()):
+        assert torch.equal(a, b)
