@@ -398,6 +398,9 @@ __device__ __forceinline__ u32x4 dma_rsrc(const void* base, uint32_t bytes) {
 // asm: the compiler does not see these loads, so it neither drains them before
 // the next LDS read (it cannot tell they write other buffers) nor counts them;
 // the kernel's own waits (slot_barrier) order them.  The asm has no outputs.
+// M0 is a reserved register, so the compiler warns that the clobber may be
+// ignored; this kernel uses M0 for nothing else (its generated code writes M0
+// only right before each of these loads).
 __device__ __forceinline__ void dma16(const u32x4& r, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
