@@ -20,13 +20,13 @@
 //    scalars; dS^T, converted to bf16 in registers, is the B operand of
 //    dQ^T += K^T dS^T (K^T staged in the transposed operand groups).  It
 //    also writes D for the second kernel.
-//  * dk/dv kernel -- one workgroup per (sequence, KV head, 64 keys), one wave
+//  * dk/dv kernel -- one workgroup per (sequence, KV head, 128 keys), one wave
 //    per 32 keys: S = Q K^T and dP = dO V^T with a lane owning one key (K and
 //    V rows held in registers for the whole kernel); P and dS in bf16 are the
 //    B operands of dV^T += dO^T P and dK^T += Q^T dS.  The loop runs over the
 //    group's query heads and over the query tiles that see the keys; each
 //    tile (Q and dO rows, both again transposed, lse, D) is staged once in
-//    LDS for the workgroup's waves.
+//    LDS for the workgroup's four waves (two of them stage it).
 // Every other shape (float32, other head dims, group size 1) runs on the
 // vector-ALU kernels at the end of the file.
 #include <algorithm>
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(NWK * 64) void attn_bwd_dkdv_kernel(
   // (tasks of four rows x one 8-d block cover every chunk of the tile once:
   // each chunk is loaded once and written both as a row and transposed)
   const uint32_t qrs = (uint32_t)heads_q * kD * 2;
-  constexpr int kTTasks = 128 / kThreads;
+  constexpr int kTTasks = (128 + kThreads - 1) / kThreads;   // 128 tasks per tile (whole waves past them idle)
   u32x4 tq[kTTasks][4], to[kTTasks][4];
   float plse = 0.f, pds = 0.f;
   auto gload = [&](int it) {
@@ -366,8 +366,18 @@ __global__ __launch_bounds__(NWK * 64) void attn_bwd_dkdv_kernel(
     const int tq0 = (wg_tile0 + it % n_qt_wg) * kQT;
     const size_t base = ((size_t)b * q_len * heads_q + h) * kD;
     const uint32_t nbytes = (uint32_t)((size_t)q_len * qrs - (size_t)h * kD * 2);
-    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc((void*)(q + base), (short)0, nbytes, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t orr = __builtin_amdgcn_make_buffer_rsrc((void*)(d_out + base), (short)0, nbytes, kRsrcWord3);
+    // (base and size through readfirstlane: the compiler did not always prove
+    // them uniform, and a descriptor in vector registers makes every load a
+    // loop over the lanes' values)
+    auto uniform_rsrc = [](const uint16_t* p, uint32_t bytes) {
+      const uint64_t a = (uint64_t)(uintptr_t)p;
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+      void* u = reinterpret_cast<void*>((uintptr_t)(((uint64_t)hi << 32) | lo));
+      return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
+    };
+    const __amdgpu_buffer_rsrc_t qr = uniform_rsrc(q + base, nbytes);
+    const __amdgpu_buffer_rsrc_t orr = uniform_rsrc(d_out + base, nbytes);
     // the tile's first row goes in the scalar offset, the lane's row in the
     // vector offset (a per-lane scalar offset would make the compiler loop
     // over its distinct values)
@@ -375,6 +385,7 @@ __global__ __launch_bounds__(NWK * 64) void attn_bwd_dkdv_kernel(
 #pragma unroll
     for (int i = 0; i < kTTasks; ++i) {
       const int c = tid + kThreads * i;
+      if (kThreads > 128 && wave * 64 + kThreads * i >= 128) break;   // whole waves (wave is uniform)
       const int r0 = vtask_row0(c);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -392,6 +403,7 @@ __global__ __launch_bounds__(NWK * 64) void attn_bwd_dkdv_kernel(
 #pragma unroll
     for (int i = 0; i < kTTasks; ++i) {
       const int c = tid + kThreads * i;
+      if (kThreads > 128 && wave * 64 + kThreads * i >= 128) break;   // whole waves (wave is uniform)
       const int r0 = vtask_row0(c);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -792,7 +804,7 @@ hipError_t launch_attn_backward(const void* q, const void* k_sel, const void* v_
                                         batch, q_len, heads_q, heads_kv, dim, scale, dq, dk_sel, dv_sel,
                                         dk_loc, dv_loc, dsum, s);
   }
-  constexpr int kNWK = 2;
+  constexpr int kNWK = 4;
   static const hipError_t attr = [] {
     hipError_t e = hipSuccess;
     auto set = [&](const void* kern, size_t bytes) {
