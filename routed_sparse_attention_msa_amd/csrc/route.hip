@@ -39,6 +39,7 @@
 // All end with the max over each document's chunks (cross-lane shuffles)
 // and over the query tokens of each sequence.
 #include <algorithm>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -541,7 +542,13 @@ struct TiledSmem {
   float rk[kMaxHeads + 1][kNB];
 };
 
-__device__ __forceinline__ int swz(int row, int seg) { return row * 128 + ((seg ^ (row & 7)) << 4); }
+// 16 B segment seg of a 128 B row, XOR-swizzled by (row / 2) % 8.  A 256 B
+// LDS bank line holds two rows; a 16-lane phase of a b128 read takes one
+// segment of 16 consecutive rows, whose 8 even and 8 odd rows then fall on
+// 8 distinct segments each, so the phase is conflict-free (with row % 8 the
+// rows r and r + 8 collided, every operand read 2-way conflicted).  A
+// 16-lane phase of the stores writes two whole rows: conflict-free too.
+__device__ __forceinline__ int swz(int row, int seg) { return row * 128 + ((seg ^ ((row >> 1) & 7)) << 4); }
 
 __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
     const uint16_t* __restrict__ q_r, const uint16_t* __restrict__ kbar,
@@ -607,22 +614,18 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
     voff[i] = (uint32_t)(c >> 3) * row_bytes + (c & 7) * 16;
   }
   u32x4 pq[4], pk[4];
-  auto gload = [&](int stage) {
+  // one of the four 16 B pieces of q and of k per thread: load for a stage,
+  // store to an LDS buffer
+  auto gload1 = [&](int stage, int i) {
     const uint32_t soff = (uint32_t)((stage >> 1) * kDim + (stage & 1) * 64) * 2;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pq[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, voff[i], soff, 0));
-      pk[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, voff[i], soff, 0));
-    }
+    pq[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, voff[i], soff, 0));
+    pk[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, voff[i], soff, 0));
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + kTiledThreads * i;
-      const int r = c >> 3, seg = c & 7;
-      *reinterpret_cast<u32x4*>(&sm.q[buf][swz(r, seg)]) = pq[i];
-      *reinterpret_cast<u32x4*>(&sm.k[buf][swz(r, seg)]) = pk[i];
-    }
+  auto lstore1 = [&](int buf, int i) {
+    const int c = tid + kTiledThreads * i;
+    const int r = c >> 3, seg = c & 7;
+    *reinterpret_cast<u32x4*>(&sm.q[buf][swz(r, seg)]) = pq[i];
+    *reinterpret_cast<u32x4*>(&sm.k[buf][swz(r, seg)]) = pk[i];
   };
 
   f32x16 acc[4][2];
@@ -631,24 +634,35 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
 
-  // chain to head hn (or, with hn == heads, apply the final scale)
+  // chain to head hn (or, with hn == heads, apply the final scale).  Every
+  // factor is read before the first multiply, so the reads' LDS latencies
+  // overlap instead of each standing between two groups of multiplies.
   auto rescale = [&](int hn) {
     float ck[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) ck[b] = sm.rk[hn][wn * 64 + b * 32 + cl];
+    f32x4 rq4[4][4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 rq4 = *reinterpret_cast<const f32x4*>(&sm.rq[hn][wm * 128 + a * 32 + 8 * q + 4 * hf]);
+      for (int q = 0; q < 4; ++q)
+        rq4[a][q] = *reinterpret_cast<const f32x4*>(&sm.rq[hn][wm * 128 + a * 32 + 8 * q + 4 * hf]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[a][b][4 * q + e] *= rq4[e] * ck[b];
-      }
-    }
+          for (int e = 0; e < 4; ++e) acc[a][b][4 * q + e] *= rq4[a][q][e] * ck[b];
   };
-  auto stage_mfma = [&](int buf) {
+  // One stage's MFMAs from LDS buffer buf.  Between them the staged
+  // registers go to buffer nbuf (no wave reads it in this stage: every wave
+  // passed the barrier after its last reads of it) and, with LOAD, are
+  // reloaded with stage nstage, one piece per k step, so the stores and
+  // loads issue while the matrix core is busy instead of after the stage.
+  auto stage_mfma = [&](int buf, int nbuf, int nstage, auto load) {
     const uint8_t* qs = sm.q[buf];
     const uint8_t* ks = sm.k[buf];
 #pragma unroll
@@ -669,30 +683,37 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[a][b] = mfma32(af[a], bfr[b], acc[a][b]);
+      lstore1(nbuf, s);
+      if constexpr (decltype(load)::value) gload1(nstage, s);
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // LDS reads of this step
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);  // LDS writes
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
+      if constexpr (decltype(load)::value) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // global loads
     }
   };
 
-  // Two stages (the halves of one head) per iteration; the previous head's
-  // chained rescale opens the iteration, in the same block as this head's
-  // MFMAs, so it can overlap them.  Loads are issued unconditionally
-  // (clamped to the last stage) so one fixed set is in flight.
+  // Two stages (the halves of one head) per iteration; the chained rescale
+  // to the next head closes it, and the next stage's global loads follow the
+  // rescale (the staged registers then hold its factors).  Loads are issued
+  // unconditionally (clamped to the last stage) so one fixed set is in flight.
   const int n_stages = 2 * heads;
-  gload(0);
-  lstore(0);
-  gload(1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) gload1(0, i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lstore1(0, i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) gload1(1, i);
   __syncthreads();
   for (int h = 0; h < heads; ++h) {
-    if (h > 0) rescale(h);
-    stage_mfma(0);
-    lstore(1);
-    gload(min(2 * h + 2, n_stages - 1));
+    stage_mfma(0, 1, min(2 * h + 2, n_stages - 1), std::true_type{});
     __syncthreads();
-    stage_mfma(1);
-    lstore(0);
-    gload(min(2 * h + 3, n_stages - 1));
+    stage_mfma(1, 0, 0, std::false_type{});
+    rescale(h + 1);                     // h + 1 == heads: the final scale
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gload1(min(2 * h + 3, n_stages - 1), i);
     __syncthreads();
   }
-  rescale(heads);
 
   // --- epilogue: max over each row block's 32 rows, then each doc's chunks ----
   const int ndw = kNB / cpd;  // documents per workgroup tile
