@@ -228,7 +228,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(
         dsf[kb][s2] = as_bf16x8(w);
       }
     // dQ^T += K^T dS^T
-    const uint8_t* tbase = &tl.kt[(hf * kVGStride + cl + (cl >> 3)) * 16];
+    const uint8_t* tbase = &tl.kt[(hf * kVGStride + vg_lane(cl)) * 16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(
         bf16x8 kt[4];
 #pragma unroll
         for (int db = 0; db < 4; ++db)
-          kt[db] = *reinterpret_cast<const bf16x8*>(tbase + ((4 * kb + 2 * s2) * kVGStride + 36 * db) * 16);
+          kt[db] = *reinterpret_cast<const bf16x8*>(tbase + ((4 * kb + 2 * s2) * kVGStride + kVGBlock * db) * 16);
 #pragma unroll
         for (int db = 0; db < 4; ++db) acc[db] = mfma32(kt[db], dsf[kb][s2], acc[db]);
       }
@@ -490,13 +490,13 @@ __global__ __launch_bounds__(NWK * 64) void attn_bwd_dkdv_kernel(
           dsf[s2] = as_bf16x8(wd);
         }
         // dV^T += dO^T P and dK^T += Q^T dS (lane (d, hf) reads its 8 queries of group 2*s2 + hf)
-        const int tb_ = (hf * kVGStride + cl + (cl >> 3)) * 16;
+        const int tb_ = (hf * kVGStride + vg_lane(cl)) * 16;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           bf16x8 ot[4], qtf[4];
 #pragma unroll
           for (int db = 0; db < 4; ++db) {
-            const int o = tb_ + ((2 * s2) * kVGStride + 36 * db) * 16;
+            const int o = tb_ + ((2 * s2) * kVGStride + kVGBlock * db) * 16;
             ot[db] = *reinterpret_cast<const bf16x8*>(&tl.ot[o]);
             qtf[db] = *reinterpret_cast<const bf16x8*>(&tl.qt[o]);
           }

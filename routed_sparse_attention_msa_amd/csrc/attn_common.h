@@ -9,7 +9,7 @@ namespace msa {
 namespace attn {
 
 constexpr int kD = 128;                 // head dim of the MFMA kernels
-constexpr int kVGStride = 144;          // 16 B units per operand-group row: 128 d + one pad unit per 8
+constexpr int kVGStride = 136;          // 16 B units per operand-group row: 128 d + one pad unit per 16
 constexpr int kKPitch = 272;            // bytes per row in LDS: 256 + 16 pad (conflict-free reads)
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -24,7 +24,16 @@ __device__ __forceinline__ int acc_row(int i, int hf) { return 8 * (i >> 2) + 4 
 // Transposed operand groups: group G = 4*kb + 2*s2 + hf holds rows
 // 32kb + 16s2 + 4hf + {0..3, 8..11} of a tile, one 16-byte unit (8 rows at
 // one d) per d, so that a lane's 8 contraction values of one MFMA are one read.
-__device__ __forceinline__ int vunit(int grp, int d) { return (grp * kVGStride + d + (d >> 3)) * 16; }
+// One pad unit follows every 16 d.  A b128 read is served 16 lanes at a time
+// from a 256 B (16-unit) bank line: the 16 lanes of a phase read 16
+// consecutive d of one group, which land on 16 distinct units.  The staging
+// stores (d = 8*dblk + 2e for dblk 0..15) land on units 8*(dblk % 2) + dblk/2
+// + 2e: distinct too.  (A pad per 8 d put d = 0 and d = 15 on one unit.)
+__device__ __forceinline__ int vunit(int grp, int d) { return (grp * kVGStride + d + (d >> 4)) * 16; }
+// Unit offset, within its group, of column d = 32*db + cl: the lane's base
+// vg_lane(cl) plus the constant kVGBlock * db.
+__device__ __forceinline__ int vg_lane(int cl) { return cl + (cl >> 4); }
+constexpr int kVGBlock = 34;
 // First row of transposed-staging task c (4 rows, one 8-d block).
 __device__ __forceinline__ int vtask_row0(int c) {
   const int grp = c >> 5, half = (c >> 4) & 1;

@@ -171,8 +171,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_decode_kernel(
       w1[1] = pair_hi(r.va[i][2], r.vb[i][2]);
       w1[2] = pair_lo(r.va[i][3], r.vb[i][3]);
       w1[3] = pair_hi(r.va[i][3], r.vb[i][3]);
-      *reinterpret_cast<u32x4*>(&vreg[pr * kVStride + seg * 8]) = w0;
-      *reinterpret_cast<u32x4*>(&vreg[pr * kVStride + seg * 8 + 4]) = w1;
+      // A lane's 32 B are two stores.  A 16-lane phase of one store covers
+      // a 256 B bank line with 16 B units: with every lane storing its
+      // first half first, lanes seg and seg + 8 would hit one unit (2-way
+      // conflict); lanes seg >= 8 store their second half first instead.
+      const bool swap = seg >= 8;
+      const int x = swap ? 4 : 0;
+      *reinterpret_cast<u32x4*>(&vreg[pr * kVStride + seg * 8 + x]) = swap ? w1 : w0;
+      *reinterpret_cast<u32x4*>(&vreg[pr * kVStride + seg * 8 + (4 - x)]) = swap ? w0 : w1;
     }
     // mask, online max, probabilities
     float mt = -INFINITY;

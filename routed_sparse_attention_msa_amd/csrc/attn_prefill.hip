@@ -53,7 +53,7 @@ constexpr float kLazy = 8.f;  // log2 headroom of the lazy running max
 
 struct PrefillSmem {
   uint8_t k[2][kKT * kKPitch];            // [key][256 B + pad]
-  uint8_t v[2][8 * kVGStride * 16];       // [group][d + d/8][8 bf16]
+  uint8_t v[2][8 * kVGStride * 16];       // [group][d + d/16][8 bf16]
 };
 
 template <int NW, int SPLIT>
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(NW * 64 * SPLIT) void attn_prefill_kernel(
     }
     // O^T += V^T P^T: lane (d, hf) reads its 8 keys of group 4kb + 2s2 + hf at
     // column d = 32db + cl, i.e. unit vunit(grp, d) = lane base + a constant.
-    const uint8_t* vbase = &sm.v[buf][(hf * kVGStride + cl + (cl >> 3)) * 16];
+    const uint8_t* vbase = &sm.v[buf][(hf * kVGStride + vg_lane(cl)) * 16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(NW * 64 * SPLIT) void attn_prefill_kernel(
         bf16x8 vf[4];
 #pragma unroll
         for (int db = 0; db < 4; ++db)
-          vf[db] = *reinterpret_cast<const bf16x8*>(vbase + ((4 * kb + 2 * s2) * kVGStride + 36 * db) * 16);
+          vf[db] = *reinterpret_cast<const bf16x8*>(vbase + ((4 * kb + 2 * s2) * kVGStride + kVGBlock * db) * 16);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int db = 0; db < 4; ++db) o[db] = mfma32(vf[db], pf[kb][s2], o[db]);
