@@ -39,7 +39,6 @@
 // All end with the max over each document's chunks (cross-lane shuffles)
 // and over the query tokens of each sequence.
 #include <algorithm>
-#include <type_traits>
 
 #include "internal.h"
 
@@ -634,35 +633,34 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
 
-  // chain to head hn (or, with hn == heads, apply the final scale).  Every
-  // factor is read before the first multiply, so the reads' LDS latencies
-  // overlap instead of each standing between two groups of multiplies.
+  // chain to head hn (or, with hn == heads, apply the final scale); the four
+  // factor reads of a row block are issued together, so their LDS latencies
+  // overlap.
   auto rescale = [&](int hn) {
     float ck[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) ck[b] = sm.rk[hn][wn * 64 + b * 32 + cl];
-    f32x4 rq4[4][4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 4; ++a) {
+      f32x4 rq4[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        rq4[a][q] = *reinterpret_cast<const f32x4*>(&sm.rq[hn][wm * 128 + a * 32 + 8 * q + 4 * hf]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
+        rq4[q] = *reinterpret_cast<const f32x4*>(&sm.rq[hn][wm * 128 + a * 32 + 8 * q + 4 * hf]);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[a][b][4 * q + e] *= rq4[a][q][e] * ck[b];
+          for (int e = 0; e < 4; ++e) acc[a][b][4 * q + e] *= rq4[q][e] * ck[b];
+    }
   };
   // One stage's MFMAs from LDS buffer buf.  Between them the staged
   // registers go to buffer nbuf (no wave reads it in this stage: every wave
-  // passed the barrier after its last reads of it) and, with LOAD, are
-  // reloaded with stage nstage, one piece per k step, so the stores and
-  // loads issue while the matrix core is busy instead of after the stage.
-  auto stage_mfma = [&](int buf, int nbuf, int nstage, auto load) {
+  // passed the barrier after its last reads of it) and are reloaded with
+  // stage nstage, one piece per k step, so the stores and loads issue while
+  // the matrix core is busy instead of after the stage, and each load has a
+  // whole stage to land before its store.
+  auto stage_mfma = [&](int buf, int nbuf, int nstage) {
     const uint8_t* qs = sm.q[buf];
     const uint8_t* ks = sm.k[buf];
 #pragma unroll
@@ -684,19 +682,18 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[a][b] = mfma32(af[a], bfr[b], acc[a][b]);
       lstore1(nbuf, s);
-      if constexpr (decltype(load)::value) gload1(nstage, s);
+      gload1(nstage, s);
       __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // LDS reads of this step
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);  // LDS writes
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
-      if constexpr (decltype(load)::value) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // global loads
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // global loads
     }
   };
 
   // Two stages (the halves of one head) per iteration; the chained rescale
-  // to the next head closes it, and the next stage's global loads follow the
-  // rescale (the staged registers then hold its factors).  Loads are issued
-  // unconditionally (clamped to the last stage) so one fixed set is in flight.
+  // to the next head closes it.  Loads are issued unconditionally (clamped to
+  // the last stage) so one fixed set is in flight.
   const int n_stages = 2 * heads;
 #pragma unroll
   for (int i = 0; i < 4; ++i) gload1(0, i);
@@ -706,12 +703,10 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
   for (int i = 0; i < 4; ++i) gload1(1, i);
   __syncthreads();
   for (int h = 0; h < heads; ++h) {
-    stage_mfma(0, 1, min(2 * h + 2, n_stages - 1), std::true_type{});
+    stage_mfma(0, 1, min(2 * h + 2, n_stages - 1));
     __syncthreads();
-    stage_mfma(1, 0, 0, std::false_type{});
+    stage_mfma(1, 0, min(2 * h + 3, n_stages - 1));
     rescale(h + 1);                     // h + 1 == heads: the final scale
-#pragma unroll
-    for (int i = 0; i < 4; ++i) gload1(min(2 * h + 3, n_stages - 1), i);
     __syncthreads();
   }
 
