@@ -160,11 +160,13 @@ def test_route_parity(batch, q_len, heads, dim, n_docs, cpd, dtype):
     assert err.max() <= 2e-5
 
 
-@pytest.mark.parametrize("batch,q_len", [(1, 1), (4, 32)])
+@pytest.mark.parametrize("batch,q_len", [(1, 1), (4, 32), (4, 512)])
 def test_route_scan_large_bank_sampled(batch, q_len):
     """The 100M-token shard's bank (195,313 documents x 8 chunks x 8 heads x 128,
-    3.2 GB bf16) in the launch configuration of the scan; the scores of sampled
-    documents against the oracle on those documents' chunks."""
+    3.2 GB bf16); the scores of sampled documents against the oracle on those
+    documents' chunks.  Up to 128 query tokens this is the streaming scan; the
+    shard's own query batch, 4 sequences x 512 tokens, runs the tiled MFMA path
+    over the whole bank (about 6.5 TFLOP, some 9 ms)."""
     case(f"route scan large bank B={batch} T={q_len} (sampled)")
     n_docs, cpd = 195313, 8
     g = torch.Generator(device=DEV)
