@@ -1,6 +1,7 @@
 """Benchmark of the MSA routed-layer hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode|interleave|backward|linear|encode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload prefill|decode|interleave|backward|linear|encode|stack]
                     [--no-cpu-baseline]
 
 A step is one pass of the whole hot path over one batch of synthetic input
@@ -28,13 +29,17 @@ already resident in HBM:
   encode  (offline encoder: 2048 documents of 256..768 tokens, ~1M tokens,
            8 KV heads x 128, bf16): chunk offsets -> encode K (document-wise
            RoPE, base 1e6) -> encode V -> encode K_r (+ norms)
+  stack   (18 routed layers at a 10M-token memory, each with its own bank of
+           19,532 docs x 512 tokens, 8192-token prefill, top-32, 32/8 heads):
+           (route -> top-k -> gather -> attention) for every layer; the banks
+           are pooled beforehand (the offline stage), timed apart
 
 Prints one JSON line.  `value` is query tokens per second of the whole step.
 W eager warm-up steps, then K eager steps with HIP events around every launch
 (on the stream the kernels run on: the per-kernel durations, `stages` and
 `roofline`, which describes the kernel with the largest share of the step),
 then the step captured once in a HIP graph and K replays timed: `ms_per_step`
-and `value` (the route, decode, interleave and linear steps; the eager figure
+and `value` (the route, decode, interleave, linear and stack steps; the eager figure
 is `ms_per_step_eager`).  The replays run the same kernels on the same data
 without the host's per-launch cost between short kernels.
 `cpu_baseline` times the float64 CPU oracle on a bounded sample of the same
@@ -76,7 +81,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", choices=["prefill", "decode", "interleave", "backward", "linear", "encode"], default="prefill")
+    p.add_argument("--workload", choices=["prefill", "decode", "interleave", "backward", "linear", "encode", "stack"],
+                   default="prefill")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     # profiling helpers (see "Profiles" in the module docstring)
@@ -190,6 +196,8 @@ STAGE_KERNELS = {
                "encode_rope": ("encode_kernel<unsigned short, true>", "encode.hip"),
                "encode": ("encode_kernel<unsigned short, false>", "encode.hip")},
     # (the two plain encode launches share one kernel; its entry is their median)
+    "stack": {"route": ("route_", "route.hip"), "topk": ("topk", "topk.hip"),
+              "gather": ("gather", "gather.hip"), "attn": ("attn_prefill", "attn_prefill.hip")},
 }
 COPY_PROBE_BYTES = 1 << 30
 
@@ -670,6 +678,176 @@ class LinearStep:
                           f"{c.batch} sequences)", "seconds_per_step": secs}
 
 
+class StackStep:
+    """The 18-layer stack at a 10M-token memory: every layer has its own bank
+    (19,532 documents x 512 tokens, 8 KV heads x 128, bf16, N(0,1) values),
+    router queries, queries and local KV (8192-token prefill), and routes
+    independently.  Each layer's raw K, V and K_r are drawn in slabs of 512
+    documents and pooled on the GPU as they are drawn (the offline stage,
+    outside the step).  One step: route -> top-32 -> gather -> attention for
+    each of the 18 layers."""
+
+    SLAB_DOCS = 512
+
+    def __init__(self, seed, dev):
+        import torch
+        import msa_inputs as mi
+        import routed_sparse_attention_msa_amd as msa
+        self.torch, self.msa, self.cfg = torch, msa, mi.STACK18
+        cfg = self.cfg
+        cpd, n_ch, hkv, d = cfg.chunks_per_doc, cfg.n_chunks, cfg.heads_kv, cfg.dim
+        e = lambda *shape, dt=torch.bfloat16: torch.empty(shape, dtype=dt, device=dev)
+        u8 = lambda n: torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+        self.layers = []
+        t0 = time.perf_counter()
+        for layer in range(cfg.layers):
+            t = mi.draw_layer(cfg, seed=seed + 1000 * layer, device=dev, with_raw=False)
+            g = torch.Generator(device=dev)
+            g.manual_seed(seed + 1000 * layer + 1)
+            L = {"q": t["q"], "k_loc": t["k_loc"], "v_loc": t["v_loc"], "q_r": t["q_r"],
+                 "kbar": e(n_ch, hkv, d), "vbar": e(n_ch, hkv, d), "kbar_r": e(n_ch, hkv, d),
+                 "knorm": e(n_ch, hkv, dt=torch.float32)}
+            for name in ("kbar", "vbar", "kbar_r"):
+                for d0 in range(0, cfg.n_doc, self.SLAB_DOCS):
+                    d1 = min(cfg.n_doc, d0 + self.SLAB_DOCS)
+                    raw = (torch.randn((d1 - d0, cfg.doc_len, hkv, d), generator=g, device=dev)
+                           * cfg.value_scale).to(torch.bfloat16)
+                    dst = L[name][d0 * cpd:d1 * cpd]
+                    if name == "kbar_r":
+                        msa.msa_pool_chunks(raw, cfg.chunk, xbar=dst, xbar_norm=L["knorm"][d0 * cpd:d1 * cpd])
+                    else:
+                        msa.msa_pool_chunks(raw, cfg.chunk, xbar=dst)
+                    del raw
+            L["out"] = torch.empty_like(t["q"])
+            L["lse"] = e(cfg.batch, cfg.heads_q, cfg.q_len, dt=torch.float32)
+            self.layers.append(L)
+            torch.cuda.synchronize()
+        self.pool_s = time.perf_counter() - t0
+        self.scores = e(cfg.batch, cfg.n_doc, dt=torch.float32)
+        self.ids = e(cfg.batch, cfg.topk, dt=torch.int32)
+        self.top = e(cfg.batch, cfg.topk, dt=torch.float32)
+        self.k_sel = e(cfg.batch, cfg.mem_len, hkv, d)
+        self.v_sel = e(cfg.batch, cfg.mem_len, hkv, d)
+        self.ws_route = u8(msa.msa_route_scores_workspace(cfg.batch, cfg.q_len, hkv, d, cfg.n_doc, cpd,
+                                                          torch.bfloat16))
+        self.ws_topk = u8(msa.msa_topk_docs_workspace(cfg.batch, cfg.n_doc, cfg.topk))
+        self.ws_attn = u8(msa.msa_sparse_attn_workspace(cfg.batch, cfg.q_len, cfg.heads_q, hkv, d, cfg.mem_len,
+                                                        cfg.loc_len, torch.bfloat16))
+        torch.cuda.synchronize()
+
+    def calls(self):
+        msa, cfg, cpd = self.msa, self.cfg, self.cfg.chunks_per_doc
+        seq = []
+        for L in self.layers:
+            seq += [
+                ("route", lambda L=L: msa.msa_route_scores(L["q_r"], L["kbar_r"], L["knorm"], cpd,
+                                                           doc_scores=self.scores, ws=self.ws_route)),
+                ("topk", lambda: msa.msa_topk_docs(self.scores, cfg.topk, topk_ids=self.ids, topk_scores=self.top,
+                                                   ws=self.ws_topk)),
+                ("gather", lambda L=L: msa.msa_gather_kv(L["kbar"], L["vbar"], self.ids, cpd, k_sel=self.k_sel,
+                                                         v_sel=self.v_sel)),
+                ("attn", lambda L=L: msa.msa_sparse_attn(L["q"], self.k_sel, self.v_sel, L["k_loc"], L["v_loc"],
+                                                         out=L["out"], lse=L["lse"], ws=self.ws_attn)),
+            ]
+        return seq
+
+    run = Step.run
+
+    def work(self, stage):
+        return {"route": work_route, "topk": work_topk, "gather": work_gather, "attn": work_attn}[stage](self.cfg)
+
+    def cpu_baseline(self):
+        """The oracle on one layer's bounded sample, scaled to the layer and then to the 18 layers."""
+        import numpy as np
+        from oracle import route_scores, sparse_attention_rows, topk_docs
+        try:
+            from threadpoolctl import threadpool_info
+            blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:  # pragma: no cover
+            blas = 1
+        cfg, L, torch = self.cfg, self.layers[0], self.torch
+        f = lambda x: x.detach().float().cpu().double().numpy()
+        rng = np.random.default_rng(0)
+        cpd = cfg.chunks_per_doc
+        secs = 0.0
+        n_route = 16
+        sample = rng.choice(cfg.n_doc, n_route, replace=False)
+        rows = torch.as_tensor((sample[:, None] * cpd + np.arange(cpd)).ravel(), device=L["kbar_r"].device)
+        kb, q_r = f(L["kbar_r"][rows]), f(L["q_r"])
+        t0 = time.perf_counter()
+        route_scores(q_r, kb, cpd)
+        secs += (time.perf_counter() - t0) * cfg.n_doc / n_route
+        self.msa.msa_route_scores(L["q_r"], L["kbar_r"], L["knorm"], cpd, doc_scores=self.scores, ws=self.ws_route)
+        self.msa.msa_topk_docs(self.scores, cfg.topk, topk_ids=self.ids, topk_scores=self.top, ws=self.ws_topk)
+        self.msa.msa_gather_kv(L["kbar"], L["vbar"], self.ids, cpd, k_sel=self.k_sel, v_sel=self.v_sel)
+        sc = f(self.scores)
+        t0 = time.perf_counter()
+        topk_docs(sc, cfg.topk)
+        secs += time.perf_counter() - t0
+        ks, vs, kl, vl, q = f(self.k_sel), f(self.v_sel), f(L["k_loc"]), f(L["v_loc"]), f(L["q"])
+        n_rows_total = cfg.q_len * cfg.heads_q
+        n_att = 256
+        g = cfg.heads_q // cfg.heads_kv
+        picks = rng.integers(0, n_rows_total, n_att)
+        t0 = time.perf_counter()
+        for r in picks:
+            h, tt = int(r % cfg.heads_q), int(r // cfg.heads_q)
+            n_loc = cfg.loc_len - cfg.q_len + tt + 1
+            keys = np.concatenate([ks[0, :, h // g], kl[0, :n_loc, h // g]])
+            vals = np.concatenate([vs[0, :, h // g], vl[0, :n_loc, h // g]])
+            sparse_attention_rows(q[0, tt, h], keys, vals, 1.0 / math.sqrt(cfg.dim))
+        secs += (time.perf_counter() - t0) * n_rows_total / n_att
+        secs *= cfg.layers
+        return {"value": cfg.q_len / secs, "unit": "query tokens/s", "cores": int(blas), "kind": "oracle",
+                "sample": (f"layer 0: route all {cfg.q_len} tokens vs {n_route}/{cfg.n_doc} docs; top-k whole; "
+                           f"attention {n_att}/{n_rows_total} rows; each stage scaled to the layer, the layer "
+                           f"to the {cfg.layers} layers"),
+                "seconds_per_step": secs}
+
+
+def main_stack(args):
+    import torch
+    print("[bench] building inputs for stack18-10M-bf16 (pooling 18 banks of 10M tokens)", file=sys.stderr,
+          flush=True)
+    step = StackStep(args.seed, "cuda:0")
+    print(f"[bench] banks pooled in {step.pool_s:.1f} s; warmup {args.warmup}", file=sys.stderr, flush=True)
+    step.run(args.warmup, events=False)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    marks = step.run(args.steps, events=True)
+    end.record()
+    torch.cuda.synchronize()
+    eager_ms = start.elapsed_time(end) / args.steps
+    print(f"[bench] timing {args.steps} graph replays", file=sys.stderr, flush=True)
+    graph_ms = graph_replay_ms(step, args.steps)
+    ms_per_step = graph_ms if graph_ms is not None else eager_ms
+    stages = stage_summary(step, marks, args.steps)
+    dom = max(stages, key=lambda k: stages[k]["ms_per_step"])
+    roof = {k: stages[dom][k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+    roof.update({"kernel": dom, "avg_launch_ms": stages[dom]["avg_launch_ms"],
+                 "traffic": measured_traffic("stack", dom)})
+    c = step.cfg
+    rec = {
+        "metric": "end-to-end query tokens/s of the 18-layer routed stack at 10M-token memory (prefill)",
+        "value": c.batch * c.q_len / (ms_per_step / 1e3), "unit": "query tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "ms_per_step_eager": eager_ms,
+        "step_timing": "hip graph replay" if graph_ms is not None else "eager", "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "stack18-10M-bf16", "layers": c.layers, "n_docs": c.n_doc, "doc_len": c.doc_len,
+                   "chunk": c.chunk, "batch": c.batch, "q_len": c.q_len, "loc_len": c.loc_len,
+                   "heads_q": c.heads_q, "heads_kv": c.heads_kv, "dim": c.dim, "topk": c.topk,
+                   "mem_len": c.mem_len, "step": "(route -> top-32 -> gather -> attention) x 18 layers",
+                   "offline_pooling_s": step.pool_s},
+        "roofline": roof, "stages": stages,
+        "cpu_baseline": None if args.no_cpu_baseline else step.cpu_baseline(),
+    }
+    print(json.dumps(rec))
+
+
 def main_linear(args):
     import torch
     print("[bench] building inputs for linear-1M-decode-bf16 (encoding 2048 document states)", file=sys.stderr,
@@ -947,6 +1125,9 @@ def main():
         return
     if args.workload == "linear":
         main_linear(args)
+        return
+    if args.workload == "stack":
+        main_stack(args)
         return
     import torch
     import msa_inputs as mi

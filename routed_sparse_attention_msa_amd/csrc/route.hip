@@ -562,8 +562,15 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
   const int wave = tid >> 6, lane = tid & 63;
   const int cl = lane & 31, hf = lane >> 5;
   const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves
-  const int row0 = blockIdx.y * kTB;
-  const int64_t col0 = (int64_t)blockIdx.x * kNB;
+  // Workgroup order: the row tiles of one column tile are consecutive, so the
+  // workgroups resident at once share a few column tiles of the bank and
+  // each bank tile comes from HBM about once (column tiles fastest streamed
+  // the whole bank once per row tile once it outgrew the last-level cache).
+  const int n_ty = (t_tot + kTB - 1) / kTB;
+  const int ty = (int)(blockIdx.x % (unsigned)n_ty);
+  const int64_t tx = blockIdx.x / (unsigned)n_ty;
+  const int row0 = ty * kTB;
+  const int64_t col0 = tx * kNB;
   const size_t row_elems = (size_t)heads * kDim;
 
   // --- per-head scale tables -------------------------------------------------
@@ -729,13 +736,13 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
   const int n_blk = t_tot / 32;
   for (int idx = tid; idx < 8 * ndw; idx += kTiledThreads) {
     const int rb = idx / ndw, dw = idx - rb * ndw;
-    const int gblk = blockIdx.y * 8 + rb;
+    const int gblk = ty * 8 + rb;
     if (gblk >= n_blk) continue;
     const int b = gblk * 32 / t_len;
     const bool start = rb == 0 || ((gblk - 1) * 32 / t_len) != b;
     if (!start) continue;
     float m = red[rb * ndw + dw];
-    for (int r2 = rb + 1; r2 < 8 && blockIdx.y * 8 + r2 < n_blk && (blockIdx.y * 8 + r2) * 32 / t_len == b; ++r2)
+    for (int r2 = rb + 1; r2 < 8 && ty * 8 + r2 < n_blk && (ty * 8 + r2) * 32 / t_len == b; ++r2)
       m = fmaxf(m, red[r2 * ndw + dw]);
     const int64_t doc = col0 / cpd + dw;
     if (doc >= n_docs) continue;
@@ -876,7 +883,7 @@ hipError_t launch_route(const void* q_r, const void* kbar_r, const float* knorm,
   hipLaunchKernelGGL(route_qnorm_kernel, dim3((unsigned)((items * 16 + 255) / 256)), dim3(256), 0, s,
                      q, (int64_t)t_tot, heads, iq);
   const bool direct = tiled_direct(q_len);
-  dim3 grid((unsigned)((n_ch + kNB - 1) / kNB), (unsigned)((t_tot + kTB - 1) / kTB));
+  const dim3 grid((unsigned)(((n_ch + kNB - 1) / kNB) * ((t_tot + kTB - 1) / kTB)));
   const size_t smem = sizeof(TiledSmem);
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(route_tiled_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
