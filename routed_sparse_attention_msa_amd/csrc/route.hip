@@ -552,7 +552,7 @@ __device__ __forceinline__ int swz(int row, int seg) { return row * 128 + ((seg 
 __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
     const uint16_t* __restrict__ q_r, const uint16_t* __restrict__ kbar,
     const float* __restrict__ knorm, const float* __restrict__ iq, int t_tot, int t_len, int heads,
-    int64_t n_ch, int64_t n_docs, int cpd, int direct, float* __restrict__ partial,
+    int64_t n_ch, int64_t n_docs, int cpd, int direct, int row_groups, float* __restrict__ partial,
     float* __restrict__ out) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   TiledSmem& sm = *reinterpret_cast<TiledSmem*>(smem_raw);
@@ -562,13 +562,26 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
   const int wave = tid >> 6, lane = tid & 63;
   const int cl = lane & 31, hf = lane >> 5;
   const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves
-  // Workgroup order: the row tiles of one column tile are consecutive, so the
-  // workgroups resident at once share a few column tiles of the bank and
-  // each bank tile comes from HBM about once (column tiles fastest streamed
-  // the whole bank once per row tile once it outgrew the last-level cache).
+  // Workgroup order.  Workgroups go to the 8 XCDs round-robin by launch
+  // index, so XCD c runs indices c, c + 8, ...; they are given one
+  // contiguous run of a tile order in which the row tiles are split into
+  // row_groups contiguous groups, each enumerated column by column with its
+  // row tiles fastest.  An XCD's run then stays inside one row group: it
+  // reads each of its column tiles of the bank into its L2 once, for all of
+  // that group's row tiles, and keeps only the group's queries resident.
+  // The bank is read row_groups times, the queries about 8 / row_groups
+  // times.  (Column tiles fastest streamed the whole bank from HBM once per
+  // row tile.)  Any order is correct; this one only places reuse.
   const int n_ty = (t_tot + kTB - 1) / kTB;
-  const int ty = (int)(blockIdx.x % (unsigned)n_ty);
-  const int64_t tx = blockIdx.x / (unsigned)n_ty;
+  const unsigned n_tx = gridDim.x / (unsigned)n_ty;
+  const unsigned n_wg = gridDim.x, xcd = blockIdx.x % 8u, per = n_wg / 8u, extra = n_wg % 8u;
+  const unsigned tile = xcd * per + min(xcd, extra) + blockIdx.x / 8u;
+  int grp = 0;
+  while (grp + 1 < row_groups && n_tx * (unsigned)((grp + 1) * n_ty / row_groups) <= tile) ++grp;
+  const int r_lo = grp * n_ty / row_groups, r_hi = (grp + 1) * n_ty / row_groups;
+  const unsigned in_grp = tile - n_tx * (unsigned)r_lo;
+  const int ty = r_lo + (int)(in_grp % (unsigned)(r_hi - r_lo));
+  const int64_t tx = in_grp / (unsigned)(r_hi - r_lo);
   const int row0 = ty * kTB;
   const int64_t col0 = tx * kNB;
   const size_t row_elems = (size_t)heads * kDim;
@@ -889,8 +902,16 @@ hipError_t launch_route(const void* q_r, const void* kbar_r, const float* knorm,
       reinterpret_cast<const void*>(route_tiled_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
       (int)smem);
   if (attr != hipSuccess) return attr;
+  // row groups: enough that one group's queries (heads * 256 B per token)
+  // take at most about 2 MiB of an XCD's 4 MB L2; a divisor of 8, at most
+  // the number of row tiles
+  const int n_ty = (t_tot + kTB - 1) / kTB;
+  int row_groups = 1;
+  while (row_groups < 8 && 2 * row_groups <= n_ty &&
+         (size_t)t_tot * heads * kDim * 2 > (size_t)row_groups * (2u << 20))
+    row_groups *= 2;
   hipLaunchKernelGGL(route_tiled_kernel, grid, dim3(kTiledThreads), smem, s, q, k, knorm, iq, t_tot,
-                     q_len, heads, n_ch, n_docs, cpd, direct ? 1 : 0, partial, doc_scores);
+                     q_len, heads, n_ch, n_docs, cpd, direct ? 1 : 0, row_groups, partial, doc_scores);
   if (!direct) {
     hipLaunchKernelGGL(route_combine_kernel, dim3((unsigned)((n_docs + 255) / 256), batch), dim3(256),
                        0, s, partial, q_len, batch, n_docs, doc_scores);
