@@ -466,14 +466,20 @@ __global__ __launch_bounds__(NWK * 64) void attn_bwd_dkdv_kernel(
           }
         }
         // visibility: a real key, and for local keys row <= shift + t; rows
-        // past the last token have lse2 = +inf (P = 0)
-        if (!__all(key_ok && (mem || kappa_row <= shift + tq0))) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int tt = tq0 + acc_row(i, hf);
-            if (!key_ok || (!mem && kappa_row > shift + tt)) s[i] = -INFINITY;
-          }
-        }
+        // past the last token have lse2 = +inf (P = 0).  A hidden element's
+        // exponent argument becomes -inf (P = 0, dS = 0) by integer masking of
+        // its bits, with no branch: a conditional assignment (to the
+        // accumulator, or a select the compiler turned back into control
+        // flow) made a branch per element, around which every dK/dV
+        // accumulator was copied out of its registers and back on every tile.
+        const unsigned masked = __all(key_ok && (mem || kappa_row <= shift + tq0)) ? 0u : 1u;   // uniform
+        const unsigned key_bad = key_ok ? 0u : 1u, local = mem ? 0u : 1u;
+        auto arg = [&](int i) {
+          const float x = fmaf(s[i], scale_log2, -l2[i]);
+          const unsigned late = kappa_row > shift + tq0 + acc_row(i, hf) ? 1u : 0u;
+          const unsigned m = 0u - (masked & (key_bad | (local & late)));        // all ones when hidden
+          return __uint_as_float((__float_as_uint(x) & ~m) | (0xFF800000u & m));
+        };
         bf16x8 pf[2], dsf[2];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
@@ -481,8 +487,8 @@ __global__ __launch_bounds__(NWK * 64) void attn_bwd_dkdv_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i0 = 8 * s2 + 2 * e;
-            const float p0 = fast_exp2(fmaf(s[i0], scale_log2, -l2[i0]));
-            const float p1 = fast_exp2(fmaf(s[i0 + 1], scale_log2, -l2[i0 + 1]));
+            const float p0 = fast_exp2(arg(i0));
+            const float p1 = fast_exp2(arg(i0 + 1));
             wp[e] = pack_bf16x2(p0, p1);
             wd[e] = pack_bf16x2(p0 * (dp[i0] - dd[i0]), p1 * (dp[i0 + 1] - dd[i0 + 1]));
           }
