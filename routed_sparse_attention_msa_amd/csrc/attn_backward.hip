@@ -201,6 +201,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(
         s[kb] = mfma32(kf[st], qf[st], s[kb]);
         dp[kb] = mfma32(vf[st], df[st], dp[kb]);
       }
+      // all sixteen operand reads before the MFMAs (otherwise each MFMA
+      // waited for its own read, issued into one reused register quad)
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
     }
     const bool mem = tile_mem(tile);
     if (mem ? kappa0 + kKT > mem_len : kappa0 + kKT > full_below) {
@@ -454,6 +458,12 @@ __global__ __launch_bounds__(NWK * 64) void attn_bwd_dkdv_kernel(
           s = mfma32(qa[st], kf[st], s);
           dp = mfma32(oa[st], vf[st], dp);
         }
+        // the operand reads ahead of the MFMAs, eight at a time (one read per
+        // MFMA made each MFMA wait for its own read)
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         float l2[16], dd[16];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
