@@ -128,6 +128,11 @@ def _route_case(batch, q_len, heads, dim, n_docs, cpd, dtype, seed, planted=None
     (1, 512, 8, 128, 64, 16, torch.bfloat16),     # 16 chunks per document
     (1, 256, 4, 128, 90, 8, torch.bfloat16),      # 4 heads
     (1, 256, 1, 128, 64, 2, torch.bfloat16),      # 1 head
+    # tiled workgroup order with several row groups (uneven where the row tiles
+    # do not divide): 10 row tiles in 4 groups, 12 in 4, 17 (the last ragged) in 8
+    (5, 512, 8, 128, 40, 8, torch.bfloat16),
+    (3, 1024, 8, 128, 36, 8, torch.bfloat16),
+    (1, 4288, 8, 128, 35, 8, torch.bfloat16),
     # MFMA stream path: odd head counts, 16 heads, one chunk per document
     (2, 32, 5, 128, 50, 8, torch.bfloat16),
     (1, 8, 16, 128, 40, 8, torch.bfloat16),
