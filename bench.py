@@ -1,7 +1,7 @@
 """Benchmark of the MSA routed-layer hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload prefill|decode|interleave|backward|linear|encode|stack]
+                    [--workload prefill|decode|interleave|backward|linear|encode|stack|scan100m]
                     [--no-cpu-baseline]
 
 A step is one pass of the whole hot path over one batch of synthetic input
@@ -9,10 +9,13 @@ already resident in HBM:
 
   prefill (default; the 1M-token bank: 2048 docs x 512 tokens, 32/8 heads,
            head dim 128, bf16, 2048-token prefill, top-16):
-      pool K, pool V, pool K_r (+norms) -> route -> top-k -> gather -> attention
+      route -> top-k -> gather -> attention; the offline stage (pool K, pool V,
+      pool K_r + norms into the bank) is timed apart in the same run and
+      reported as `offline_pool` (encoded tokens/s, HBM fraction)
   decode  (the same bank; 32 sequences x 1 token, 4096 cached tokens, top-16):
       route -> top-k -> gather -> split-KV attention (the bank is pooled once,
-      outside the timed region, as the offline stage of the pipeline)
+      outside the timed region, as the offline stage of the pipeline); the
+      routing scan is also timed warm and cold (`route_scan_warm_cold`)
   interleave (the prefill workload with 3 routing rounds, Memory Interleave at
            kernel level: each round routes its own planted router query and
            keeps the top-16 documents no earlier round took; the 48 documents'
@@ -29,12 +32,21 @@ already resident in HBM:
   encode  (offline encoder: 2048 documents of 256..768 tokens, ~1M tokens,
            8 KV heads x 128, bf16): chunk offsets -> encode K (document-wise
            RoPE, base 1e6) -> encode V -> encode K_r (+ norms)
+  scan100m (one GPU's share of a 100M-token memory: 195,313 docs x 512
+           tokens around 1024 cluster centres, a 3.2 GB router bank in HBM, the
+           pooled content K/V in pinned host memory; 4 x 512 router query
+           tokens, top-16): route -> top-k -> host-tier fetch of the 64
+           selected docs; also a routing sweep over T_tot = 1 .. 2048 query
+           tokens (`route_sweep`) and the host-tier fetch in both modes, alone
+           and overlapped with the next step's routing (`host_tier`)
   stack   (18 routed layers at a 10M-token memory, each with its own bank of
            19,532 docs x 512 tokens, 8192-token prefill, top-32, 32/8 heads):
            (route -> top-k -> gather -> attention) for every layer; the banks
            are pooled beforehand (the offline stage), timed apart
 
-Prints one JSON line.  `value` is query tokens per second of the whole step.
+Prints one JSON line.  `value` is query tokens per second of the whole step
+(for the default workload the online step, route -> top-k -> gather ->
+attention; its offline pooling has its own entry).
 W eager warm-up steps, then K eager steps with HIP events around every launch
 (on the stream the kernels run on: the per-kernel durations, `stages` and
 `roofline`, which describes the kernel with the largest share of the step),
@@ -81,7 +93,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", choices=["prefill", "decode", "interleave", "backward", "linear", "encode", "stack"],
+    p.add_argument("--workload", choices=["prefill", "decode", "interleave", "backward", "linear", "encode", "stack",
+                                          "scan100m"],
                    default="prefill")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -144,6 +157,18 @@ def work_attn(cfg):
     return {"bound": "mfma" if flops / b > ridge else "hbm", "bytes": b, "flops": flops}
 
 
+def host_threads():
+    """Host threads the oracle runs on: `cores` is the BLAS thread count (its
+    matrix products use them; its element-wise NumPy work runs on one), beside
+    the cores this process may use (os.sched_getaffinity)."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    return {"cores": int(blas), "blas_threads": int(blas), "affinity_cores": len(os.sched_getaffinity(0))}
+
+
 def roofline_entry(work, ms):
     s = ms / 1e3
     if work["bound"] == "mfma":
@@ -196,6 +221,7 @@ STAGE_KERNELS = {
                "encode_rope": ("encode_kernel<unsigned short, true>", "encode.hip"),
                "encode": ("encode_kernel<unsigned short, false>", "encode.hip")},
     # (the two plain encode launches share one kernel; its entry is their median)
+    "scan100m": {"route": ("route_", "route.hip"), "topk": ("topk", "topk.hip"), "fetch": ("gather", "gather.hip")},
     "stack": {"route": ("route_", "route.hip"), "topk": ("topk", "topk.hip"),
               "gather": ("gather", "gather.hip"), "attn": ("attn_prefill", "attn_prefill.hip")},
 }
@@ -386,10 +412,6 @@ class Step:
         """(stage, callable) in step order."""
         msa, t, cfg, c = self.msa, self.t, self.cfg, self.cfg.chunk
         seq = []
-        if self.workload == "prefill":
-            seq += [("pool", lambda: msa.msa_pool_chunks(t["k"], c, xbar=self.kbar)),
-                    ("pool", lambda: msa.msa_pool_chunks(t["v"], c, xbar=self.vbar)),
-                    ("pool", lambda: msa.msa_pool_chunks(t["k_r"], c, xbar=self.kbar_r, xbar_norm=self.knorm))]
         if self.workload == "interleave":
             seq += [("rounds", lambda: msa.msa_route_rounds(t["q_r_rounds"], self.kbar_r, self.knorm,
                                                             cfg.chunks_per_doc, cfg.topk, topk_ids=self.ids,
@@ -408,9 +430,16 @@ class Step:
         ]
         return seq
 
-    def run(self, steps, events):
+    def pool_calls(self):
+        """The offline stage (S1): pool K, V and K_r (+ norms) into the bank."""
+        msa, t, c = self.msa, self.t, self.cfg.chunk
+        return [("pool", lambda: msa.msa_pool_chunks(t["k"], c, xbar=self.kbar)),
+                ("pool", lambda: msa.msa_pool_chunks(t["v"], c, xbar=self.vbar)),
+                ("pool", lambda: msa.msa_pool_chunks(t["k_r"], c, xbar=self.kbar_r, xbar_norm=self.knorm))]
+
+    def run(self, steps, events, seq=None):
         torch = self.torch
-        seq = self.calls()
+        seq = self.calls() if seq is None else seq
         marks = []
         for _ in range(steps):
             for stage, fn in seq:
@@ -476,11 +505,6 @@ class EncodeStep:
 
     def cpu_baseline(self):
         from oracle import encode_docs
-        try:
-            from threadpoolctl import threadpool_info
-            blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        except Exception:  # pragma: no cover
-            blas = 1
         # every document: about 10 s of float64 work on the host
         docs = range(self.N_DOCS)
         secs, rows = 0.0, 0
@@ -492,7 +516,7 @@ class EncodeStep:
                 t0 = time.perf_counter()
                 encode_docs(xs, [0, b - a], self.CHUNK, rope)
                 secs += time.perf_counter() - t0
-        return {"value": rows / secs, "unit": "encoded tokens/s", "cores": int(blas), "kind": "oracle",
+        return {"value": rows / secs, "unit": "encoded tokens/s", **host_threads(), "kind": "oracle",
                 "sample": f"the whole step: {self.N_DOCS} documents ({rows} rows) x 3 tensors",
                 "seconds_per_step": secs}
 
@@ -551,11 +575,6 @@ class BackwardStep:
     def cpu_baseline(self):
         import numpy as np
         from oracle import sparse_attention_backward
-        try:
-            from threadpoolctl import threadpool_info
-            blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        except Exception:  # pragma: no cover
-            blas = 1
         c = self.cfg
         f = lambda x: x.detach().float().cpu().double().numpy()
         # one KV group (its 4 query heads) of the 8, scaled to all of them
@@ -566,7 +585,7 @@ class BackwardStep:
         sparse_attention_backward(*args, scale=1.0 / math.sqrt(c.dim))
         secs = (time.perf_counter() - t0) * c.heads_kv
         tokens = c.batch * c.q_len
-        return {"value": tokens / secs, "unit": "query tokens/s", "cores": int(blas), "kind": "oracle",
+        return {"value": tokens / secs, "unit": "query tokens/s", **host_threads(), "kind": "oracle",
                 "sample": f"backward of 1 of {c.heads_kv} KV groups (all tokens), scaled to all groups; "
                           "the forward not timed",
                 "seconds_per_step": secs}
@@ -655,11 +674,6 @@ class LinearStep:
     def cpu_baseline(self):
         import numpy as np
         from oracle import gated_delta_rule, inject_states, route_scores, topk_docs
-        try:
-            from threadpoolctl import threadpool_info
-            blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        except Exception:  # pragma: no cover
-            blas = 1
         c = self.cfg
         f = lambda x: x.detach().float().cpu().double().numpy()
         # the whole step (the selected documents' states copied to the host first, untimed)
@@ -673,7 +687,7 @@ class LinearStep:
         s_ext = inject_states(st, np.arange(c.batch * c.topk).reshape(c.batch, c.topk))
         gated_delta_rule(f(self.q), f(self.k), f(self.v), f(self.g), f(self.beta), initial_state=s_ext)
         secs += time.perf_counter() - t0
-        return {"value": c.batch * c.q_len / secs, "unit": "query tokens/s", "cores": int(blas), "kind": "oracle",
+        return {"value": c.batch * c.q_len / secs, "unit": "query tokens/s", **host_threads(), "kind": "oracle",
                 "sample": "the whole step (route over all documents, top-k, state sum and the step for all "
                           f"{c.batch} sequences)", "seconds_per_step": secs}
 
@@ -760,11 +774,6 @@ class StackStep:
         """The oracle on one layer's bounded sample, scaled to the layer and then to the 18 layers."""
         import numpy as np
         from oracle import route_scores, sparse_attention_rows, topk_docs
-        try:
-            from threadpoolctl import threadpool_info
-            blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        except Exception:  # pragma: no cover
-            blas = 1
         cfg, L, torch = self.cfg, self.layers[0], self.torch
         f = lambda x: x.detach().float().cpu().double().numpy()
         rng = np.random.default_rng(0)
@@ -798,11 +807,274 @@ class StackStep:
             sparse_attention_rows(q[0, tt, h], keys, vals, 1.0 / math.sqrt(cfg.dim))
         secs += (time.perf_counter() - t0) * n_rows_total / n_att
         secs *= cfg.layers
-        return {"value": cfg.q_len / secs, "unit": "query tokens/s", "cores": int(blas), "kind": "oracle",
+        return {"value": cfg.q_len / secs, "unit": "query tokens/s", **host_threads(), "kind": "oracle",
                 "sample": (f"layer 0: route all {cfg.q_len} tokens vs {n_route}/{cfg.n_doc} docs; top-k whole; "
                            f"attention {n_att}/{n_rows_total} rows; each stage scaled to the layer, the layer "
                            f"to the {cfg.layers} layers"),
                 "seconds_per_step": secs}
+
+
+class ScanStep:
+    """The routing scan at one GPU's share of a 100M-token memory
+    (scan-100M-share-bf16): 195,313 documents x 512 tokens drawn around 1024
+    Gaussian cluster centres (sigma 0.3) in slabs and pooled on the GPU into a
+    3.2 GB router bank (the offline stage, timed apart); the pooled content
+    K-bar / V-bar in pinned host memory (6.4 GB, doc-major).  One step: route
+    4 x 512 router query tokens over the whole bank -> top-16 per sequence ->
+    fetch of the 64 selected documents' content from the host tier (the GPU
+    reads the pinned rows directly)."""
+
+    SLAB = 2048
+
+    def __init__(self, seed, dev):
+        import torch
+        import msa_inputs as mi
+        import routed_sparse_attention_msa_amd as msa
+        self.torch, self.msa, self.mi, self.cfg, self.dev = torch, msa, mi, mi.SCAN100M, dev
+        cfg = self.cfg
+        cpd, n_ch, hkv, d = cfg.chunks_per_doc, cfg.n_chunks, cfg.heads_kv, cfg.dim
+        e = lambda *shape, dt=torch.bfloat16: torch.empty(shape, dtype=dt, device=dev)
+        self.kbar_r = e(n_ch, hkv, d)
+        self.knorm = e(n_ch, hkv, dt=torch.float32)
+        t0 = time.perf_counter()
+        for d0 in range(0, cfg.n_doc, self.SLAB):
+            d1 = min(cfg.n_doc, d0 + self.SLAB)
+            raw = mi.draw_scan_bank_slab(cfg, seed, d0, d1, dev)
+            msa.msa_pool_chunks(raw, cfg.chunk, xbar=self.kbar_r[d0 * cpd:d1 * cpd],
+                                xbar_norm=self.knorm[d0 * cpd:d1 * cpd])
+            del raw
+        torch.cuda.synchronize()
+        self.pool_s = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        self.hk = torch.empty((n_ch, hkv, d), dtype=torch.bfloat16, pin_memory=True)
+        self.hv = torch.empty((n_ch, hkv, d), dtype=torch.bfloat16, pin_memory=True)
+        for d0 in range(0, cfg.n_doc, 16384):
+            d1 = min(cfg.n_doc, d0 + 16384)
+            k, v = mi.draw_scan_content_slab(cfg, seed, d0, d1, dev)
+            self.hk[d0 * cpd:d1 * cpd].copy_(k)
+            self.hv[d0 * cpd:d1 * cpd].copy_(v)
+        torch.cuda.synchronize()
+        self.host_s = time.perf_counter() - t0
+        self.q_r = mi.draw_scan_queries(cfg, seed, dev)
+        self.bufs = [self._buffers() for _ in range(2)]     # two sets: the two-stream pipeline
+        self.scores, self.ids, self.top = self.bufs[0]["scores"], self.bufs[0]["ids"], self.bufs[0]["top"]
+        self.k_sel, self.v_sel = self.bufs[0]["k_sel"], self.bufs[0]["v_sel"]
+        torch.cuda.synchronize()
+
+    def _buffers(self):
+        torch, msa, cfg, dev = self.torch, self.msa, self.cfg, self.dev
+        e = lambda *shape, dt=torch.bfloat16: torch.empty(shape, dtype=dt, device=dev)
+        u8 = lambda n: torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+        return {"scores": e(cfg.batch, cfg.n_doc, dt=torch.float32), "ids": e(cfg.batch, cfg.topk, dt=torch.int32),
+                "top": e(cfg.batch, cfg.topk, dt=torch.float32),
+                "k_sel": e(cfg.batch, cfg.mem_len, cfg.heads_kv, cfg.dim),
+                "v_sel": e(cfg.batch, cfg.mem_len, cfg.heads_kv, cfg.dim),
+                "ws_route": u8(msa.msa_route_scores_workspace(cfg.batch, cfg.q_len, cfg.heads_kv, cfg.dim,
+                                                              cfg.n_doc, cfg.chunks_per_doc, torch.bfloat16)),
+                "ws_topk": u8(msa.msa_topk_docs_workspace(cfg.batch, cfg.n_doc, cfg.topk))}
+
+    def _route(self, B):
+        return lambda: self.msa.msa_route_scores(self.q_r, self.kbar_r, self.knorm, self.cfg.chunks_per_doc,
+                                                 doc_scores=B["scores"], ws=B["ws_route"])
+
+    def _topk(self, B):
+        return lambda: self.msa.msa_topk_docs(B["scores"], self.cfg.topk, topk_ids=B["ids"], topk_scores=B["top"],
+                                              ws=B["ws_topk"])
+
+    def _fetch(self, B, host_memcpy=False):
+        return lambda: self.msa.msa_gather_kv(self.hk, self.hv, B["ids"], self.cfg.chunks_per_doc,
+                                              k_sel=B["k_sel"], v_sel=B["v_sel"], host_memcpy=host_memcpy)
+
+    def calls(self):
+        B = self.bufs[0]
+        return [("route", self._route(B)), ("topk", self._topk(B)), ("fetch", self._fetch(B))]
+
+    run = Step.run
+
+    def work(self, stage):
+        cfg = self.cfg
+        if stage == "fetch":      # the selected rows cross the host link once and land in HBM once
+            b = 2 * cfg.batch * cfg.mem_len * cfg.heads_kv * cfg.dim * 2
+            return {"bound": "hbm", "bytes": b + cfg.batch * cfg.topk * 4, "flops": 0}
+        return {"route": work_route, "topk": work_topk}[stage](cfg)
+
+    def sweep(self, reps):
+        """Routing over the 3.2 GB bank at T_tot = 1, 4, 32, 128, 512, 2048 query
+        tokens: where the scan is HBM-bound (T_tot below the ridge, about 315)
+        and where it turns MFMA-bound."""
+        torch, msa, cfg = self.torch, self.msa, self.cfg
+        import dataclasses as dc
+        q = self.q_r
+        shapes = [(1, 1, q[:1, :1]), (4, 1, q[:, :1]), (32, 1, q[:, :8].reshape(32, 1, 8, 128)),
+                  (128, 1, q[:, :32].reshape(128, 1, 8, 128)), (4, 128, q[:, :128]), (4, 512, q)]
+        out = []
+        for b, t, qq in shapes:
+            qq = qq.contiguous()
+            sc = torch.empty((b, cfg.n_doc), dtype=torch.float32, device=self.dev)
+            ws = torch.empty(max(16, msa.msa_route_scores_workspace(b, t, cfg.heads_kv, cfg.dim, cfg.n_doc,
+                                                                    cfg.chunks_per_doc, torch.bfloat16)),
+                             dtype=torch.uint8, device=self.dev)
+            fn = lambda: msa.msa_route_scores(qq, self.kbar_r, self.knorm, cfg.chunks_per_doc, doc_scores=sc, ws=ws)
+            fn()
+            ms = time_launches(fn, reps)
+            w = work_route(dc.replace(cfg, batch=b, q_len=t))
+            hbm = roofline_entry(dict(w, bound="hbm"), ms)
+            mf = roofline_entry(dict(w, bound="mfma"), ms)
+            out.append({"t_tot": b * t, "batch": b, "q_len": t, "path": "scan" if b * t <= 128 else "tiled",
+                        "bound": w["bound"], "ms": ms, "bytes": w["bytes"], "flops": w["flops"],
+                        "GB/s": hbm["achieved"], "frac_hbm": hbm["frac"], "TFLOP/s": mf["achieved"],
+                        "frac_mfma": mf["frac"]})
+            print(f"[bench] sweep T_tot={b * t}: {ms:.3f} ms, {hbm['achieved']:.0f} GB/s ({hbm['frac']:.3f} of HBM), "
+                  f"{mf['achieved']:.0f} TFLOP/s", file=sys.stderr, flush=True)
+        return out
+
+    def host_tier(self, reps, units=8):
+        """The host-tier fetch of the 64 selected documents (2 MiB of pooled
+        content over the host link), both modes, alone and overlapped with the
+        next unit's routing on a second stream."""
+        import torch
+        B = self.bufs[0]
+        self._route(B)()
+        self._topk(B)()
+        torch.cuda.synchronize()
+        nbytes = self.work("fetch")["bytes"]
+        res = {"bytes": nbytes}
+        for mode, memcpy in (("zero_copy", False), ("memcpy", True)):
+            fn = self._fetch(B, memcpy)
+            fn()
+            walls = []
+
+            def timed():
+                t0 = time.perf_counter()
+                fn()
+                walls.append(time.perf_counter() - t0)
+            ms = time_launches(timed, reps)
+            res[mode] = {"fetch_ms": ms, "GB/s_pcie_inclusive": nbytes / (ms / 1e3) / 1e9,
+                         "host_call_ms": 1e3 * _median(walls)}
+        # pipelines of `units` steps over two streams: unit u routes on stream u % 2
+        # while the host waits for unit u-1's ids and its copies run
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+
+        def pipeline(fetch_mode):
+            cur = torch.cuda.current_stream()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(cur)
+            for st in streams:
+                st.wait_stream(cur)
+            for u in range(units + 1):
+                if u < units:
+                    Bu = self.bufs[u % 2]
+                    with torch.cuda.stream(streams[u % 2]):
+                        self._route(Bu)()
+                        self._topk(Bu)()
+                        if fetch_mode == "zero_copy":
+                            self._fetch(Bu)()
+                if u > 0 and fetch_mode == "memcpy":
+                    with torch.cuda.stream(streams[(u - 1) % 2]):
+                        self._fetch(self.bufs[(u - 1) % 2], True)()
+            for st in streams:
+                cur.wait_stream(st)
+            b.record(cur)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / units
+
+        pipeline(None)
+        base = _median([pipeline(None) for _ in range(3)])
+        res["pipeline"] = {"units": units, "route_topk_ms_per_unit": base}
+        for mode in ("zero_copy", "memcpy"):
+            pipeline(mode)
+            with_f = _median([pipeline(mode) for _ in range(3)])
+            res["pipeline"][f"with_{mode}_fetch_ms_per_unit"] = with_f
+            res["pipeline"][f"{mode}_fetch_exposed_ms"] = with_f - base
+        return res
+
+    def cpu_baseline(self):
+        """The oracle on a bounded sample: all 4 x 512 tokens routed against 4096
+        of the 195,313 documents (scaled to the bank), the whole top-k on the
+        GPU's scores, and the gather of the 64 selected documents from the host
+        bank."""
+        import numpy as np
+        from oracle import gather_kv, route_scores, topk_docs
+        torch, cfg = self.torch, self.cfg
+        f = lambda x: x.detach().float().cpu().double().numpy()
+        rng = np.random.default_rng(0)
+        cpd = cfg.chunks_per_doc
+        n_route = 4096
+        sample = rng.choice(cfg.n_doc, n_route, replace=False)
+        rows = torch.as_tensor((sample[:, None] * cpd + np.arange(cpd)).ravel(), device=self.dev)
+        kb, q_r = f(self.kbar_r[rows]), f(self.q_r)
+        secs = 0.0
+        t0 = time.perf_counter()
+        route_scores(q_r, kb, cpd)
+        secs += (time.perf_counter() - t0) * cfg.n_doc / n_route
+        self._route(self.bufs[0])()
+        self._topk(self.bufs[0])()
+        sc = f(self.bufs[0]["scores"])
+        t0 = time.perf_counter()
+        ids, _ = topk_docs(sc, cfg.topk)
+        secs += time.perf_counter() - t0
+        raw = lambda t: t.view(torch.int16).numpy()
+        t0 = time.perf_counter()
+        gather_kv(raw(self.hk), raw(self.hv), ids, cpd)
+        secs += time.perf_counter() - t0
+        tokens = cfg.batch * cfg.q_len
+        return {"value": tokens / secs, "unit": "query tokens/s", **host_threads(), "kind": "oracle",
+                "sample": (f"route all {tokens} tokens vs {n_route}/{cfg.n_doc} docs (scaled to the bank); "
+                           "top-k whole; gather of the 64 selected docs from the host bank"),
+                "seconds_per_step": secs}
+
+
+def main_scan(args):
+    import torch
+    print("[bench] building inputs for scan-100M-share-bf16 (pooling a 3.2 GB router bank, 6.4 GB of pinned "
+          "host content)", file=sys.stderr, flush=True)
+    step = ScanStep(args.seed, "cuda:0")
+    print(f"[bench] bank pooled in {step.pool_s:.1f} s, host content in {step.host_s:.1f} s; warmup {args.warmup}",
+          file=sys.stderr, flush=True)
+    step.run(args.warmup, events=False)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    marks = step.run(args.steps, events=True)
+    end.record()
+    torch.cuda.synchronize()
+    eager_ms = start.elapsed_time(end) / args.steps
+    print(f"[bench] timing {args.steps} graph replays", file=sys.stderr, flush=True)
+    graph_ms = graph_replay_ms(step, args.steps)
+    ms_per_step = graph_ms if graph_ms is not None else eager_ms
+    stages = stage_summary(step, marks, args.steps)
+    dom = max(stages, key=lambda k: stages[k]["ms_per_step"])
+    roof = {k: stages[dom][k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+    roof.update({"kernel": dom, "avg_launch_ms": stages[dom]["avg_launch_ms"],
+                 "traffic": measured_traffic("scan100m", dom)})
+    print("[bench] routing sweep over the 3.2 GB bank", file=sys.stderr, flush=True)
+    sweep = step.sweep(max(5, min(args.steps, 20)))
+    print("[bench] host-tier fetch, alone and overlapped", file=sys.stderr, flush=True)
+    host = step.host_tier(max(5, min(args.steps, 20)))
+    c = step.cfg
+    rec = {
+        "metric": "query tokens/s of the routing scan at a 100M-token share (3.2 GB router bank) with the "
+                  "host-tier fetch of the selected documents",
+        "value": c.batch * c.q_len / (ms_per_step / 1e3), "unit": "query tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "ms_per_step_eager": eager_ms,
+        "step_timing": "hip graph replay" if graph_ms is not None else "eager", "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "scan-100M-share-bf16", "n_docs": c.n_doc, "doc_len": c.doc_len, "chunk": c.chunk,
+                   "n_chunks": c.n_chunks, "heads_kv": c.heads_kv, "dim": c.dim, "batch": c.batch, "q_len": c.q_len,
+                   "topk": c.topk, "clusters": c.clusters, "cluster_sigma": c.cluster_sigma,
+                   "step": "route 4 x 512 tokens over the bank -> top-16 -> host-tier fetch (zero-copy) of the "
+                           "64 selected docs",
+                   "offline_pooling_s": step.pool_s},
+        "roofline": roof, "stages": stages, "route_sweep": sweep, "host_tier": host,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = step.cpu_baseline()
+    print(json.dumps(rec))
 
 
 def main_stack(args):
@@ -963,6 +1235,53 @@ def graph_replay_ms(step, steps, warmup=2):
     return a.elapsed_time(b) / steps
 
 
+def _median(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2]
+
+
+def time_launches(fn, reps, before=None):
+    """Median duration (ms) of `fn`'s launches over `reps` repetitions, with HIP
+    events on the current stream around each; `before` runs untimed ahead of
+    every repetition."""
+    import torch
+    marks = []
+    for _ in range(reps):
+        if before is not None:
+            before()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        marks.append((a, b))
+    torch.cuda.synchronize()
+    return _median([a.elapsed_time(b) for a, b in marks])
+
+
+def route_scan_warm_cold(step, cfg, reps):
+    """The decode step's routing scan over the 1M-token bank (32 MiB of K_r-bar,
+    which the 256 MB MALL holds between steps) timed warm (back to back) and
+    cold (a 512 MiB read between repetitions evicts it; a read, because the
+    write-back of a written flush would land inside the timed scan)."""
+    import torch
+    msa = step.msa
+    fn = lambda: msa.msa_route_scores(step.t["q_r"], step.kbar_r, step.knorm, cfg.chunks_per_doc,
+                                      doc_scores=step.scores, ws=step.ws_route)
+    flush = torch.ones((512 << 20) // 4, dtype=torch.float32, device=step.kbar_r.device)
+    sink = torch.empty((), dtype=torch.float32, device=step.kbar_r.device)
+    w = work_route(cfg)
+    out = {}
+    for name, before in (("warm", None), ("cold", lambda: torch.sum(flush, out=sink))):
+        fn()
+        ms = time_launches(fn, max(reps, 10), before)
+        e = roofline_entry(dict(w, bound="hbm"), ms)
+        out[name] = {"ms": ms, "GB/s": e["achieved"], "frac_hbm": e["frac"]}
+    out["bytes"] = w["bytes"]
+    del flush
+    return out
+
+
 def stage_summary(step, marks, steps):
     per, counts = {}, {}
     for stage, a, b in marks:
@@ -1030,25 +1349,22 @@ def cpu_baseline(step, cfg, workload):
     import numpy as np
     import torch
     from oracle import pool_chunks_mean, route_scores, sparse_attention_rows, topk_docs, topk_docs_excluding
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        blas = 1
     f = lambda x: x.detach().float().cpu().double().numpy()
     rng = np.random.default_rng(0)
     cpd = cfg.chunks_per_doc
     secs = 0.0
     parts = []
+    pool_secs = None
     if workload == "prefill":
+        # the offline stage, reported beside the step (not part of it)
         n_pool = 64
+        pool_secs = 0.0
         docs = torch.as_tensor(rng.choice(cfg.n_doc, n_pool, replace=False), device=step.t["k"].device)
         for name in ("k", "v", "k_r"):
             x = f(step.t[name][docs])
             t0 = time.perf_counter()
             pool_chunks_mean(x, cfg.chunk)
-            secs += (time.perf_counter() - t0) * cfg.n_doc / n_pool
-        parts.append(f"pool {n_pool}/{cfg.n_doc} docs x3 tensors")
+            pool_secs += (time.perf_counter() - t0) * cfg.n_doc / n_pool
     n_route = 256
     sample = rng.choice(cfg.n_doc, n_route, replace=False)
     rows = torch.as_tensor((sample[:, None] * cpd + np.arange(cpd)).ravel(), device=step.kbar_r.device)
@@ -1096,9 +1412,13 @@ def cpu_baseline(step, cfg, workload):
     secs += (time.perf_counter() - t0) * n_rows_total / n_att
     parts.append(f"attention {n_att}/{n_rows_total} rows")
     tokens = cfg.batch * cfg.q_len
-    return {"value": tokens / secs, "unit": "query tokens/s", "cores": int(blas), "kind": "oracle",
-            "sample": "; ".join(parts) + "; each stage's time scaled to the full step",
-            "seconds_per_step": secs}
+    rec = {"value": tokens / secs, "unit": "query tokens/s", **host_threads(), "kind": "oracle",
+           "sample": "; ".join(parts) + "; each stage's time scaled to the full step",
+           "seconds_per_step": secs}
+    if pool_secs is not None:
+        rec["offline_pool_seconds"] = pool_secs
+        rec["offline_pool_sample"] = f"pool {n_pool}/{cfg.n_doc} docs x3 tensors, scaled to the bank"
+    return rec
 
 
 def main():
@@ -1128,6 +1448,9 @@ def main():
         return
     if args.workload == "stack":
         main_stack(args)
+        return
+    if args.workload == "scan100m":
+        main_scan(args)
         return
     import torch
     import msa_inputs as mi
@@ -1180,7 +1503,25 @@ def main():
     roof["traffic"] = measured_traffic(args.workload, dom)
 
     tokens = cfg.batch * cfg.q_len
-    online_ms = sum(stages[s]["ms_per_step"] for s in stages if s != "pool")
+    offline = None
+    if args.workload == "prefill":
+        # S1, the offline stage of the pipeline, timed apart from the step
+        print(f"[bench] timing {args.steps} passes of the offline pooling", file=sys.stderr, flush=True)
+        pool_seq = step.pool_calls()
+        step.run(1, events=False, seq=pool_seq)
+        torch.cuda.synchronize()
+        pmarks = step.run(args.steps, events=True, seq=pool_seq)
+        torch.cuda.synchronize()
+        pool_ms = [a.elapsed_time(b) for _, a, b in pmarks]
+        avg = sum(pool_ms) / len(pool_ms)
+        offline = roofline_entry(work_pool(cfg, with_norm=False), avg)
+        offline.update({"kernel": "pool", "avg_launch_ms": avg, "launches_per_pass": 3,
+                        "ms_per_pass": 3 * avg, "traffic": measured_traffic("prefill", "pool"),
+                        "encoded_tokens_per_s": cfg.n_doc * cfg.doc_len / (3 * avg / 1e3),
+                        "pass": "pool K, pool V, pool K_r (+ norms): 2048 docs x 512 tokens each"})
+    route_cold = None
+    if args.workload == "decode":
+        route_cold = route_scan_warm_cold(step, cfg, args.steps)
     rec = {
         "metric": ("query tokens/s at 1M-token memory (routing-scan GB/s + sparse-attn TFLOP/s in stages)"
                    if rounds == 1 else
@@ -1202,14 +1543,18 @@ def main():
                    "batch": cfg.batch, "q_len": cfg.q_len, "loc_len": cfg.loc_len, "heads_q": cfg.heads_q,
                    "heads_kv": cfg.heads_kv, "dim": cfg.dim, "topk": cfg.topk, "rounds": rounds,
                    "mem_len": rounds * cfg.mem_len,
-                   "step": {"prefill": "pool K,V,K_r -> route -> top-k -> gather -> attention",
+                   "step": {"prefill": "route -> top-k -> gather -> attention (the bank pooled offline, "
+                                       "timed apart: offline_pool)",
                             "decode": "route -> top-k -> gather -> split-KV attention",
                             "interleave": f"(route -> top-k excluding earlier picks) x{rounds} -> gather -> "
                                           "attention"}[args.workload]},
         "roofline": roof,
         "stages": stages,
-        "online_tokens_per_s": tokens / (online_ms / 1e3),
     }
+    if offline is not None:
+        rec["offline_pool"] = offline
+    if route_cold is not None:
+        rec["route_scan_warm_cold"] = route_cold
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(step, cfg, args.workload)

@@ -20,9 +20,11 @@
  *   are device pointers unless stated otherwise, 16-byte aligned.
  * - The caller owns every buffer.  No entry point allocates device memory;
  *   scratch space comes from the caller's workspace (`ws`, `ws_bytes`),
- *   sized by the matching *_workspace call.  (The host-tier gather keeps one
- *   small library-owned device flag word and side stream per device, created
- *   on first use and kept until the process ends.)
+ *   sized by the matching *_workspace call (or by msa_workspace_size).
+ *   (msa_gather_kv keeps a library-owned side stream per device and a pool
+ *   of staging slots, each a few events, a pinned id buffer and one device
+ *   error word; a call takes a slot of its own for its duration.  They are
+ *   created on first use and kept until the process ends.)
  * - `stream` is a hipStream_t passed as void*; NULL means the null stream.
  *   All work is enqueued on it, asynchronously; a call returns before the
  *   GPU has finished unless stated otherwise.
@@ -31,8 +33,10 @@
  *   but not implemented).  A failed launch returns MSA_ERR_HIP.  Faults of
  *   enqueued work surface at the caller's next synchronisation, as in HIP.
  *   msa_last_error() then returns a description (thread-local).
- * - No C++ exception crosses this boundary.  Calls are thread-safe; calls on
- *   one stream execute in order.
+ * - No C++ exception crosses this boundary.  Calls are thread-safe: the
+ *   only state shared between calls is the host tier's staging pool, taken
+ *   and returned under a lock that is never held while waiting.  Calls on one
+ *   stream execute in order.
  * - dtype MSA_BF16 stores bfloat16 bit patterns (uint16); MSA_F32 stores
  *   IEEE float32.  Arithmetic is float32 in either case; rounding to the
  *   storage dtype is round-to-nearest-even.
@@ -60,11 +64,47 @@ typedef enum msa_dtype { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
 #define MSA_GATHER_CHECKED 1     /* synchronise and report out-of-range ids as MSA_ERR_INVALID */
 #define MSA_GATHER_HOST_MEMCPY 2 /* host tier: per-document hipMemcpyAsync on a side stream     */
 
+/* Operations, for msa_workspace_size. */
+typedef enum msa_op {
+  MSA_OP_POOL_CHUNKS = 0,
+  MSA_OP_ROUTE_SCORES = 1,
+  MSA_OP_TOPK_DOCS = 2,
+  MSA_OP_GATHER_KV = 3,
+  MSA_OP_SPARSE_ATTN = 4,
+  MSA_OP_SPARSE_ATTN_BACKWARD = 5,
+  MSA_OP_ROUTE_ROUNDS = 6,
+  MSA_OP_TOPK_DOCS_EXCLUDING = 7,
+  MSA_OP_ENCODE_DOCS = 8,
+  MSA_OP_GDN_STATE_SUM = 9,
+  MSA_OP_GATED_DELTA_RULE = 10
+} msa_op;
+
 /* Version of this ABI (bumped on any incompatible change). */
 int msa_abi_version(void);
 
 /* Text describing the last non-OK status returned on the calling thread. */
 const char* msa_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Workspace size of one call, by operation (MSA README "Inference Pipeline":
+ * the three stages whose steps the entry points below implement).  One
+ * entry point in front of the per-operation *_workspace calls, for callers
+ * that size scratch generically.
+ *
+ * op     an msa_op value
+ * dims   the integer arguments of the operation's *_workspace call, in that
+ *        call's order, the dtype given as its msa_dtype value:
+ *          MSA_OP_ROUTE_SCORES          {batch, q_len, heads, dim, n_docs, chunks_per_doc, dtype}
+ *          MSA_OP_TOPK_DOCS(_EXCLUDING) {batch, n_docs, k}
+ *          MSA_OP_ROUTE_ROUNDS          {rounds, batch, q_len, heads, dim, n_docs, chunks_per_doc, k, dtype}
+ *          MSA_OP_SPARSE_ATTN(_BACKWARD) {batch, q_len, heads_q, heads_kv, dim, mem_len, loc_len, dtype}
+ *        The other operations use no scratch: *bytes = 0 whatever dims hold.
+ * ndims  the number of entries in dims; a count that does not match the
+ *        operation, an unknown op or an argument the per-operation call
+ *        rejects returns MSA_ERR_INVALID.
+ * bytes  output: the workspace size in bytes (host pointer).
+ * ---------------------------------------------------------------------- */
+msa_status msa_workspace_size(int32_t op, const int64_t* dims, int32_t ndims, size_t* bytes);
 
 /* ------------------------------------------------------------------------
  * S1  Chunk-mean pooling (MSA README "Overall Design"; "Inference Pipeline",
@@ -220,14 +260,24 @@ msa_status msa_route_rounds(const void* q_r, const void* kbar_r, const float* kb
  *              the GPU reads directly over the host link (no host round
  *              trip), or, with MSA_GATHER_HOST_MEMCPY, which is copied per
  *              selected document with hipMemcpyAsync on a library side stream
- *              after the ids are read back (the caller's stream then waits on
- *              that copy; the call blocks until the ids are on the host).
+ *              after the ids are read back.  In that mode the call records an
+ *              event on `stream`, copies the ids to the host on the side
+ *              stream once that event has passed, and blocks until they
+ *              arrive: it waits for the work queued on `stream` before the
+ *              call, nothing later and no other stream (so work queued on
+ *              another stream beforehand, e.g. the next routing, keeps the
+ *              GPU busy during the wait and the copies).  `stream` then waits
+ *              on the copies.
  * topk_ids     [batch, k] int32 device pointer
  * k_sel, v_sel [batch, k*C, heads_kv, dim] device outputs
  * flags        0 or MSA_GATHER_CHECKED | MSA_GATHER_HOST_MEMCPY.
  * Ids outside [0, n_docs) never cause an out-of-bounds read: their rows are
- * written as zeros.  With MSA_GATHER_CHECKED the call synchronises `stream`
- * and returns MSA_ERR_INVALID if any id was out of range.
+ * written as zeros.  With MSA_GATHER_CHECKED the call waits for `stream` up
+ * to its own gather and returns MSA_ERR_INVALID if any id was out of range
+ * (each call has its own error word).  In MSA_GATHER_HOST_MEMCPY mode an id
+ * out of range returns MSA_ERR_INVALID before any copy is enqueued.  Requires
+ * n_docs*chunks_per_doc rows in kbar and vbar; the library cannot see their
+ * length, so the caller guarantees it.
  * ---------------------------------------------------------------------- */
 msa_status msa_gather_kv(const void* kbar, const void* vbar, int32_t src_on_host,
                          const int32_t* topk_ids, int32_t batch, int32_t k, int64_t n_docs,

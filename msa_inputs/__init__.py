@@ -37,7 +37,7 @@ import torch
 __all__ = [
     "LayerConfig", "TINY", "PREFILL", "DECODE", "SCAN100M", "STACK18", "CONFIGS",
     "scaled", "draw_tiny", "draw_layer", "plant_router_queries", "rope_rotate",
-    "draw_scan_bank_slab", "draw_scan_queries",
+    "draw_scan_bank_slab", "draw_scan_queries", "draw_scan_content_slab",
 ]
 
 
@@ -255,9 +255,25 @@ def draw_scan_bank_slab(cfg, seed, doc0, doc1, device):
     gen = torch.Generator(device=device)
     gen.manual_seed(seed * 1_000_003 + doc0 + 1)
     n = doc1 - doc0
-    eps = torch.randn((n, cfg.doc_len, cfg.heads_kv, cfg.dim), generator=gen, device=device)
-    x = centres[doc_cluster[doc0:doc1]][:, None] + cfg.cluster_sigma * eps
+    x = torch.randn((n, cfg.doc_len, cfg.heads_kv, cfg.dim), generator=gen, device=device)
+    # in place (one float32 temporary): sigma * eps, then + centre -- the same
+    # float32 operations, in the same order, as centre + sigma * eps
+    x.mul_(cfg.cluster_sigma).add_(centres[doc_cluster[doc0:doc1]][:, None])
     return _store(x, cfg, device)
+
+
+def draw_scan_content_slab(cfg, seed, doc0, doc1, device):
+    """Pooled content K-bar and V-bar rows of documents [doc0, doc1) for the
+    large bank's host tier: N(0, value_scale^2) drawn directly at the pooled
+    shape [(doc1-doc0)*C, H_kv, d] (the bank stores only pooled content; its
+    values do not enter the routing), rounded to the storage dtype.  Each slab
+    has its own generator stream (seed, doc0)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed * 1_000_003 + 2_000_000_000 + doc0)
+    shape = ((doc1 - doc0) * cfg.chunks_per_doc, cfg.heads_kv, cfg.dim)
+    k = _store(_randn(gen, shape, device, cfg.value_scale), cfg, device)
+    v = _store(_randn(gen, shape, device, cfg.value_scale), cfg, device)
+    return k, v
 
 
 def draw_scan_queries(cfg, seed, device):

@@ -15,6 +15,7 @@ of ``include/msa.h``; this package is its thin Python binding:
     msa_sparse_attn_backward its gradients (training through the routed layer)
     msa_gdn_state_sum        linear-layer variant: sum of the selected documents' states
     msa_gated_delta_rule       and the gated delta rule from that initial state
+    msa_workspace_size       scratch bytes of any of these calls, by operation code
 """
 
 from ._lib import (  # noqa: F401
@@ -38,5 +39,6 @@ from ._lib import (  # noqa: F401
     msa_topk_docs,
     msa_topk_docs_excluding,
     msa_topk_docs_workspace,
+    msa_workspace_size,
     SIGNATURES,
 )

@@ -20,12 +20,16 @@ MSA_OK, MSA_ERR_INVALID, MSA_ERR_UNSUPPORTED, MSA_ERR_HIP = 0, 1, 2, 3
 MSA_F32, MSA_BF16 = 0, 1
 MSA_GATHER_CHECKED = 1
 MSA_GATHER_HOST_MEMCPY = 2
+(MSA_OP_POOL_CHUNKS, MSA_OP_ROUTE_SCORES, MSA_OP_TOPK_DOCS, MSA_OP_GATHER_KV, MSA_OP_SPARSE_ATTN,
+ MSA_OP_SPARSE_ATTN_BACKWARD, MSA_OP_ROUTE_ROUNDS, MSA_OP_TOPK_DOCS_EXCLUDING, MSA_OP_ENCODE_DOCS,
+ MSA_OP_GDN_STATE_SUM, MSA_OP_GATED_DELTA_RULE) = range(11)
 
 # Every entry point declared in include/msa.h: name -> (restype, argtypes).
 _STATUS = c_int
 SIGNATURES = {
     "msa_abi_version": (c_int, []),
     "msa_last_error": (ctypes.c_char_p, []),
+    "msa_workspace_size": (_STATUS, [c_int32, POINTER(c_int64), c_int32, POINTER(c_size_t)]),
     "msa_pool_chunks": (_STATUS, [c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_int32, c_int32,
                                   c_int32, c_int, c_void_p]),
     "msa_chunk_offsets": (_STATUS, [c_void_p, c_int64, c_int32, c_void_p, c_void_p]),
@@ -117,6 +121,12 @@ def _dev(t, name, dtype=None, ndim=None):
     return t
 
 
+def _shape(t, name, shape):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -133,6 +143,15 @@ def _workspace(nbytes, device, ws):
     elif ws.numel() * ws.element_size() < nbytes:
         raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, needs {nbytes}")
     return ws, ws.numel() * ws.element_size()
+
+
+def msa_workspace_size(op, dims):
+    """Workspace bytes of operation ``op`` (an MSA_OP_* code) for the integer
+    arguments ``dims`` of its *_workspace call (the dtype as its MSA_* code)."""
+    arr = (c_int64 * max(1, len(dims)))(*[int(d) for d in dims])
+    n = c_size_t(0)
+    _check(lib().msa_workspace_size(int(op), arr, len(dims), ctypes.byref(n)))
+    return n.value
 
 
 # ---------------------------------------------------------------------------
@@ -238,6 +257,7 @@ def msa_route_scores(q_r, kbar_r, kbar_r_norm, chunks_per_doc, doc_scores=None, 
     if doc_scores is None:
         doc_scores = torch.empty((batch, n_docs), dtype=torch.float32, device=q_r.device)
     _dev(doc_scores, "doc_scores", dtype=torch.float32)
+    _shape(doc_scores, "doc_scores", (batch, n_docs))
     nbytes = msa_route_scores_workspace(batch, q_len, heads, dim, n_docs, chunks_per_doc, q_r.dtype)
     ws, ws_bytes = _workspace(nbytes, q_r.device, ws)
     _check(lib().msa_route_scores(_ptr(q_r), _ptr(kbar_r), _ptr(kbar_r_norm), batch, q_len, heads, dim,
@@ -263,10 +283,12 @@ def msa_topk_docs(doc_scores, k, topk_ids=None, topk_scores=None, with_scores=Tr
     if topk_ids is None:
         topk_ids = torch.empty((batch, k), dtype=torch.int32, device=doc_scores.device)
     _dev(topk_ids, "topk_ids", dtype=torch.int32)
+    _shape(topk_ids, "topk_ids", (batch, k))
     if with_scores and topk_scores is None:
         topk_scores = torch.empty((batch, k), dtype=torch.float32, device=doc_scores.device)
     if topk_scores is not None:
         _dev(topk_scores, "topk_scores", dtype=torch.float32)
+        _shape(topk_scores, "topk_scores", (batch, k))
     ws, ws_bytes = _workspace(msa_topk_docs_workspace(batch, n_docs, k), doc_scores.device, ws)
     _check(lib().msa_topk_docs(_ptr(doc_scores), batch, n_docs, k, _ptr(topk_ids), _ptr(topk_scores),
                                _ptr(ws), ws_bytes, _stream(doc_scores.device)))
@@ -371,8 +393,12 @@ def msa_gather_kv(kbar, vbar, topk_ids, chunks_per_doc, k_sel=None, v_sel=None, 
     if vbar.dtype != kbar.dtype or vbar.shape != kbar.shape or vbar.is_cuda != kbar.is_cuda:
         raise ValueError("kbar and vbar must match")
     _dev(topk_ids, "topk_ids", dtype=torch.int32, ndim=2)
+    if kbar.dim() != 3:
+        raise ValueError(f"kbar must be [n_docs*C, heads_kv, dim], got {tuple(kbar.shape)}")
     n_ch, heads_kv, dim = kbar.shape
     batch, k = topk_ids.shape
+    if chunks_per_doc <= 0 or n_ch % chunks_per_doc:
+        raise ValueError(f"the bank's {n_ch} rows are not a whole number of {chunks_per_doc}-chunk documents")
     n_docs = n_ch // chunks_per_doc
     shape = (batch, k * chunks_per_doc, heads_kv, dim)
     dev = topk_ids.device
@@ -382,6 +408,8 @@ def msa_gather_kv(kbar, vbar, topk_ids, chunks_per_doc, k_sel=None, v_sel=None, 
         v_sel = torch.empty(shape, dtype=kbar.dtype, device=dev)
     _dev(k_sel, "k_sel", dtype=kbar.dtype)
     _dev(v_sel, "v_sel", dtype=kbar.dtype)
+    _shape(k_sel, "k_sel", shape)
+    _shape(v_sel, "v_sel", shape)
     flags = (MSA_GATHER_CHECKED if checked else 0) | (MSA_GATHER_HOST_MEMCPY if host_memcpy else 0)
     _check(lib().msa_gather_kv(_ptr(kbar), _ptr(vbar), 1 if on_host else 0, _ptr(topk_ids), batch, k,
                                n_docs, chunks_per_doc, heads_kv, dim, _dtype_code(kbar), _ptr(k_sel),
@@ -426,10 +454,12 @@ def msa_sparse_attn(q, k_sel, v_sel, k_loc, v_loc, scale=None, out=None, lse=Non
     if out is None:
         out = torch.empty_like(q)
     _dev(out, "out", dtype=q.dtype)
+    _shape(out, "out", q.shape)
     if with_lse and lse is None:
         lse = torch.empty((batch, heads_q, q_len), dtype=torch.float32, device=q.device)
     if lse is not None:
         _dev(lse, "lse", dtype=torch.float32)
+        _shape(lse, "lse", (batch, heads_q, q_len))
     nbytes = msa_sparse_attn_workspace(batch, q_len, heads_q, heads_kv, dim, mem_len, loc_len, q.dtype)
     ws, ws_bytes = _workspace(nbytes, q.device, ws)
     _check(lib().msa_sparse_attn(_ptr(q), _ptr(k_sel), _ptr(v_sel), mem_len, _ptr(k_loc), _ptr(v_loc),

@@ -4,8 +4,11 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cstdarg>
 #include <cstdio>
+#include <map>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -44,35 +47,78 @@ bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
     if (!(cond)) return fail(MSA_ERR_INVALID, __VA_ARGS__);    \
   } while (0)
 
-// Library-owned, per-device resources for the host tier.  Created on first
-// use, kept until the process ends.
-struct DeviceRes {
-  int* err_flag = nullptr;
-  hipStream_t side = nullptr;
-  hipEvent_t copy_done = nullptr;
-  int32_t* host_ids = nullptr;
+// Library-owned, per-device resources of the host tier and of the checked
+// gather.  Each device has one side stream and a pool of staging slots; a
+// call takes a slot for its own use (events, a pinned id buffer, an error
+// word), so concurrent calls never share one.  The pool lock is held only to
+// take or return a slot, never across a wait.  Objects are created on first
+// use, owned through unique_ptr (their addresses never move) and kept until
+// the process ends.
+struct Slot {
+  hipEvent_t ready = nullptr;    // recorded on the caller's stream when the call starts
+  hipEvent_t on_host = nullptr;  // the ids (or the error word) have reached the host
+  hipEvent_t done = nullptr;     // the slot's host-tier copies have finished
+  int32_t* host_ids = nullptr;   // pinned
   size_t host_ids_cap = 0;
+  int* dev_flag = nullptr;       // device error word of a checked gather
+  int* host_flag = nullptr;      // pinned copy of it
 };
-std::mutex g_res_mutex;
-std::vector<DeviceRes> g_res;
 
-msa_status device_res(DeviceRes** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
-  std::lock_guard<std::mutex> lock(g_res_mutex);
-  if ((int)g_res.size() <= dev) g_res.resize(dev + 1);
-  DeviceRes& r = g_res[dev];
-  if (r.err_flag == nullptr) {
-    if ((e = hipMalloc(&r.err_flag, sizeof(int))) != hipSuccess) return hip_status(e, "hipMalloc(flag)");
-    if ((e = hipStreamCreateWithFlags(&r.side, hipStreamNonBlocking)) != hipSuccess)
-      return hip_status(e, "hipStreamCreate");
-    if ((e = hipEventCreateWithFlags(&r.copy_done, hipEventDisableTiming)) != hipSuccess)
-      return hip_status(e, "hipEventCreate");
-  }
-  *out = &r;
+struct DeviceRes {
+  hipStream_t side = nullptr;
+  std::vector<std::unique_ptr<Slot>> free_slots;
+};
+
+std::mutex g_res_mutex;
+std::map<int, std::unique_ptr<DeviceRes>> g_res;
+
+msa_status new_slot(std::unique_ptr<Slot>* out) {
+  auto slot = std::make_unique<Slot>();
+  hipError_t e;
+  for (hipEvent_t* ev : {&slot->ready, &slot->on_host, &slot->done})
+    if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return hip_status(e, "hipEventCreate");
+  if ((e = hipMalloc(&slot->dev_flag, sizeof(int))) != hipSuccess) return hip_status(e, "hipMalloc(flag)");
+  if ((e = hipHostMalloc(&slot->host_flag, sizeof(int), hipHostMallocDefault)) != hipSuccess)
+    return hip_status(e, "hipHostMalloc(flag)");
+  *out = std::move(slot);
   return MSA_OK;
 }
+
+// A slot of the current device, returned to its pool when the guard ends.
+class SlotGuard {
+ public:
+  msa_status acquire() {
+    hipError_t e = hipGetDevice(&dev_);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    {
+      std::lock_guard<std::mutex> lock(g_res_mutex);
+      std::unique_ptr<DeviceRes>& r = g_res[dev_];
+      if (!r) r = std::make_unique<DeviceRes>();
+      if (r->side == nullptr &&
+          (e = hipStreamCreateWithFlags(&r->side, hipStreamNonBlocking)) != hipSuccess)
+        return hip_status(e, "hipStreamCreate");
+      side_ = r->side;
+      if (!r->free_slots.empty()) {
+        slot_ = std::move(r->free_slots.back());
+        r->free_slots.pop_back();
+        return MSA_OK;
+      }
+    }
+    return new_slot(&slot_);  // created outside the lock
+  }
+  ~SlotGuard() {
+    if (!slot_) return;
+    std::lock_guard<std::mutex> lock(g_res_mutex);
+    g_res[dev_]->free_slots.push_back(std::move(slot_));
+  }
+  Slot* slot() { return slot_.get(); }
+  hipStream_t side() const { return side_; }
+
+ private:
+  int dev_ = 0;
+  hipStream_t side_ = nullptr;
+  std::unique_ptr<Slot> slot_;
+};
 
 // Device-visible address of pinned host memory, or an error for pageable memory.
 msa_status host_device_ptr(const void* p, const void** dptr) {
@@ -355,28 +401,38 @@ msa_status msa_gather_kv(const void* kbar, const void* vbar, int32_t src_on_host
   hipError_t e;
 
   if (src_on_host && (flags & MSA_GATHER_HOST_MEMCPY)) {
-    // Per-document copies on the side stream: the ids must be on the host first.
+    // Per-document copies on the side stream; the host must know the ids first.
     const void* dk;
     const void* dv;
     msa_status st = host_device_ptr(kbar, &dk);
     if (st != MSA_OK) return st;
     if ((st = host_device_ptr(vbar, &dv)) != MSA_OK) return st;
-    DeviceRes* res = nullptr;
-    if ((st = device_res(&res)) != MSA_OK) return st;
-    std::lock_guard<std::mutex> lock(g_res_mutex);
+    SlotGuard guard;
+    if ((st = guard.acquire()) != MSA_OK) return st;
+    Slot* sl = guard.slot();
+    hipStream_t side = guard.side();
     const size_t n_ids = (size_t)batch * k;
-    if (res->host_ids_cap < n_ids) {
-      if (res->host_ids) (void)hipHostFree(res->host_ids);
-      res->host_ids = nullptr;
-      if ((e = hipHostMalloc(&res->host_ids, n_ids * sizeof(int32_t), hipHostMallocDefault)) != hipSuccess)
+    if (sl->host_ids_cap < n_ids) {
+      if (sl->host_ids) (void)hipHostFree(sl->host_ids);
+      sl->host_ids = nullptr;
+      sl->host_ids_cap = 0;
+      if ((e = hipHostMalloc(&sl->host_ids, n_ids * sizeof(int32_t), hipHostMallocDefault)) != hipSuccess)
         return hip_status(e, "hipHostMalloc(ids)");
-      res->host_ids_cap = n_ids;
+      sl->host_ids_cap = n_ids;
     }
-    if ((e = hipMemcpyAsync(res->host_ids, topk_ids, n_ids * sizeof(int32_t), hipMemcpyDeviceToHost, s)) != hipSuccess)
+    // The ids are final once the work already queued on `s` has run: mark that
+    // point with an event and bring the ids back on the side stream, so the
+    // host waits for exactly that work (not for anything queued on `s` later,
+    // nor for other threads' calls).
+    if ((e = hipEventRecord(sl->ready, s)) != hipSuccess) return hip_status(e, "event record");
+    if ((e = hipStreamWaitEvent(side, sl->ready, 0)) != hipSuccess) return hip_status(e, "side wait");
+    if ((e = hipMemcpyAsync(sl->host_ids, topk_ids, n_ids * sizeof(int32_t), hipMemcpyDeviceToHost, side)) !=
+        hipSuccess)
       return hip_status(e, "ids D2H");
-    if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_status(e, "ids sync");
+    if ((e = hipEventRecord(sl->on_host, side)) != hipSuccess) return hip_status(e, "event record");
+    if ((e = hipEventSynchronize(sl->on_host)) != hipSuccess) return hip_status(e, "ids wait");
     for (size_t i = 0; i < n_ids; ++i) {
-      const int64_t id = res->host_ids[i];
+      const int64_t id = sl->host_ids[i];
       if (id < 0 || id >= n_docs)
         return fail(MSA_ERR_INVALID, "document id %lld at position %zu out of range [0, %lld)",
                     (long long)id, i, (long long)n_docs);
@@ -384,17 +440,17 @@ msa_status msa_gather_kv(const void* kbar, const void* vbar, int32_t src_on_host
     const char* hk = static_cast<const char*>(kbar);
     const char* hv = static_cast<const char*>(vbar);
     for (size_t i = 0; i < n_ids; ++i) {
-      const size_t src = (size_t)res->host_ids[i] * doc_bytes;
+      const size_t src = (size_t)sl->host_ids[i] * doc_bytes;
       const size_t dst = i * doc_bytes;
-      if ((e = hipMemcpyAsync(static_cast<char*>(k_sel) + dst, hk + src, doc_bytes,
-                              hipMemcpyHostToDevice, res->side)) != hipSuccess)
+      if ((e = hipMemcpyAsync(static_cast<char*>(k_sel) + dst, hk + src, doc_bytes, hipMemcpyHostToDevice,
+                              side)) != hipSuccess)
         return hip_status(e, "K fetch");
-      if ((e = hipMemcpyAsync(static_cast<char*>(v_sel) + dst, hv + src, doc_bytes,
-                              hipMemcpyHostToDevice, res->side)) != hipSuccess)
+      if ((e = hipMemcpyAsync(static_cast<char*>(v_sel) + dst, hv + src, doc_bytes, hipMemcpyHostToDevice,
+                              side)) != hipSuccess)
         return hip_status(e, "V fetch");
     }
-    if ((e = hipEventRecord(res->copy_done, res->side)) != hipSuccess) return hip_status(e, "event record");
-    if ((e = hipStreamWaitEvent(s, res->copy_done, 0)) != hipSuccess) return hip_status(e, "stream wait");
+    if ((e = hipEventRecord(sl->done, side)) != hipSuccess) return hip_status(e, "event record");
+    if ((e = hipStreamWaitEvent(s, sl->done, 0)) != hipSuccess) return hip_status(e, "stream wait");
     return MSA_OK;
   }
 
@@ -405,24 +461,25 @@ msa_status msa_gather_kv(const void* kbar, const void* vbar, int32_t src_on_host
     if (st != MSA_OK) return st;
     if ((st = host_device_ptr(vbar, &src_v)) != MSA_OK) return st;
   }
-  int* flag = nullptr;
-  if (flags & MSA_GATHER_CHECKED) {
-    DeviceRes* res = nullptr;
-    msa_status st = device_res(&res);
-    if (st != MSA_OK) return st;
-    flag = res->err_flag;
-    if ((e = hipMemsetAsync(flag, 0, sizeof(int), s)) != hipSuccess) return hip_status(e, "flag clear");
+  if (!(flags & MSA_GATHER_CHECKED)) {
+    e = msa::launch_gather(src_k, src_v, topk_ids, batch, k, n_docs, chunks_per_doc, row_bytes, k_sel,
+                           v_sel, nullptr, s);
+    return hip_status(e, "msa_gather_kv launch");
   }
-  e = msa::launch_gather(src_k, src_v, topk_ids, batch, k, n_docs, chunks_per_doc, row_bytes, k_sel,
-                         v_sel, flag, s);
+  // Checked: this call's own error word, cleared, raised by the kernel, read back.
+  SlotGuard guard;
+  msa_status st = guard.acquire();
+  if (st != MSA_OK) return st;
+  Slot* sl = guard.slot();
+  if ((e = hipMemsetAsync(sl->dev_flag, 0, sizeof(int), s)) != hipSuccess) return hip_status(e, "flag clear");
+  e = msa::launch_gather(src_k, src_v, topk_ids, batch, k, n_docs, chunks_per_doc, row_bytes, k_sel, v_sel,
+                         sl->dev_flag, s);
   if (e != hipSuccess) return hip_status(e, "msa_gather_kv launch");
-  if (flag != nullptr) {
-    int h_flag = 0;
-    if ((e = hipMemcpyAsync(&h_flag, flag, sizeof(int), hipMemcpyDeviceToHost, s)) != hipSuccess)
-      return hip_status(e, "flag read");
-    if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_status(e, "flag sync");
-    if (h_flag != 0) return fail(MSA_ERR_INVALID, "a document id was outside [0, %lld)", (long long)n_docs);
-  }
+  if ((e = hipMemcpyAsync(sl->host_flag, sl->dev_flag, sizeof(int), hipMemcpyDeviceToHost, s)) != hipSuccess)
+    return hip_status(e, "flag read");
+  if ((e = hipEventRecord(sl->on_host, s)) != hipSuccess) return hip_status(e, "event record");
+  if ((e = hipEventSynchronize(sl->on_host)) != hipSuccess) return hip_status(e, "flag wait");
+  if (*sl->host_flag != 0) return fail(MSA_ERR_INVALID, "a document id was outside [0, %lld)", (long long)n_docs);
   return MSA_OK;
 }
 
@@ -436,6 +493,13 @@ static msa_status check_attn(int32_t batch, int32_t q_len, int32_t heads_q, int3
   CHECK_ARG(loc_len >= q_len, "loc_len %d must be >= q_len %d", loc_len, q_len);
   CHECK_ARG(dim <= 256, "dim %d above 256 is not supported", dim);
   CHECK_ARG(((size_t)dim * dtype_size(dt)) % 16 == 0, "dim*sizeof(dtype) must be a multiple of 16");
+  // The kernels address one sequence's memory, local and query rows through
+  // 32-bit buffer offsets: each span must stay below 4 GiB.
+  const int64_t kv_row = (int64_t)heads_kv * dim * (int64_t)dtype_size(dt);
+  const int64_t q_row = (int64_t)heads_q * dim * (int64_t)dtype_size(dt);
+  CHECK_ARG((int64_t)mem_len * kv_row < ((int64_t)1 << 32) && (int64_t)loc_len * kv_row < ((int64_t)1 << 32) &&
+                (int64_t)q_len * q_row < ((int64_t)1 << 32),
+            "one sequence's memory, local or query rows span 4 GiB or more");
   return MSA_OK;
 }
 
@@ -506,6 +570,55 @@ msa_status msa_sparse_attn_backward(const void* q, const void* k_sel, const void
                                               d_k_sel, d_v_sel, d_k_loc, d_v_loc, ws,
                                               static_cast<hipStream_t>(stream)),
                     "msa_sparse_attn_backward launch");
+}
+
+// ---------------------------------------------------------------------------
+// Workspace sizing by operation: dims are the per-operation call's integer
+// arguments in order (the dtype as its msa_dtype value).
+static bool fits_i32(int64_t v) { return v >= INT32_MIN && v <= INT32_MAX; }
+
+msa_status msa_workspace_size(int32_t op, const int64_t* dims, int32_t ndims, size_t* bytes) {
+  CHECK_ARG(bytes != nullptr, "bytes is null");
+  CHECK_ARG(ndims >= 0 && (ndims == 0 || dims != nullptr), "dims missing");
+  auto need = [&](int n) { return ndims == n; };
+  auto i32 = [&](int i) { return (int32_t)dims[i]; };
+  for (int i = 0; i < ndims; ++i) {
+    // n_docs (an int64_t argument) may exceed int32; it is range-checked by the op
+    const bool wide = (op == MSA_OP_ROUTE_SCORES && i == 4) || (op == MSA_OP_TOPK_DOCS && i == 1) ||
+                      (op == MSA_OP_TOPK_DOCS_EXCLUDING && i == 1) || (op == MSA_OP_ROUTE_ROUNDS && i == 5);
+    CHECK_ARG(wide || fits_i32(dims[i]), "dims[%d] = %lld is out of the int32 range", i, (long long)dims[i]);
+  }
+  switch (op) {
+    case MSA_OP_POOL_CHUNKS:
+    case MSA_OP_ENCODE_DOCS:
+    case MSA_OP_GATHER_KV:
+    case MSA_OP_GDN_STATE_SUM:
+    case MSA_OP_GATED_DELTA_RULE:
+      *bytes = 0;  // these operations use no scratch
+      return MSA_OK;
+    case MSA_OP_ROUTE_SCORES:
+      CHECK_ARG(need(7), "MSA_OP_ROUTE_SCORES takes 7 dims (got %d)", ndims);
+      return msa_route_scores_workspace(i32(0), i32(1), i32(2), i32(3), dims[4], i32(5), (msa_dtype)i32(6),
+                                        bytes);
+    case MSA_OP_TOPK_DOCS:
+    case MSA_OP_TOPK_DOCS_EXCLUDING:
+      CHECK_ARG(need(3), "MSA_OP_TOPK_DOCS takes 3 dims (got %d)", ndims);
+      return msa_topk_docs_workspace(i32(0), dims[1], i32(2), bytes);
+    case MSA_OP_ROUTE_ROUNDS:
+      CHECK_ARG(need(9), "MSA_OP_ROUTE_ROUNDS takes 9 dims (got %d)", ndims);
+      return msa_route_rounds_workspace(i32(0), i32(1), i32(2), i32(3), i32(4), dims[5], i32(6), i32(7),
+                                        (msa_dtype)i32(8), bytes);
+    case MSA_OP_SPARSE_ATTN:
+      CHECK_ARG(need(8), "MSA_OP_SPARSE_ATTN takes 8 dims (got %d)", ndims);
+      return msa_sparse_attn_workspace(i32(0), i32(1), i32(2), i32(3), i32(4), i32(5), i32(6), (msa_dtype)i32(7),
+                                       bytes);
+    case MSA_OP_SPARSE_ATTN_BACKWARD:
+      CHECK_ARG(need(8), "MSA_OP_SPARSE_ATTN_BACKWARD takes 8 dims (got %d)", ndims);
+      return msa_sparse_attn_backward_workspace(i32(0), i32(1), i32(2), i32(3), i32(4), i32(5), i32(6),
+                                                (msa_dtype)i32(7), bytes);
+    default:
+      return fail(MSA_ERR_INVALID, "unknown operation %d", op);
+  }
 }
 
 // ---------------------------------------------------------------------------

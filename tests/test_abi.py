@@ -149,6 +149,75 @@ def test_attn_validation():
                                0, None) == L.MSA_ERR_INVALID
 
 
+def test_attn_rejects_spans_of_4gib():
+    """One sequence's memory or local rows must span less than 4 GiB (the
+    kernels' buffer offsets are 32-bit)."""
+    lib = msa.lib()
+    p = ctypes.c_void_p(256)
+    n = ctypes.c_size_t(0)
+    big = 1 << 21                       # 2^21 rows x 8 heads x 128 x 2 B = 4 GiB
+    assert lib.msa_sparse_attn_workspace(1, 16, 32, 8, 128, big, 16, L.MSA_BF16, ctypes.byref(n)) == L.MSA_ERR_INVALID
+    assert "4 GiB" in _err()
+    assert lib.msa_sparse_attn(p, p, p, 0, p, p, big, 1, 16, 32, 8, 128, 0.1, L.MSA_BF16, p, None, None, 0,
+                               None) == L.MSA_ERR_INVALID
+    assert lib.msa_sparse_attn_backward_workspace(1, 16, 32, 8, 128, 16, big, L.MSA_BF16,
+                                                  ctypes.byref(n)) == L.MSA_ERR_INVALID
+    assert lib.msa_sparse_attn_workspace(1, 16, 32, 8, 128, big - 1, 16, L.MSA_BF16, ctypes.byref(n)) == L.MSA_OK
+
+
+def _ws(op, dims):
+    arr = (ctypes.c_int64 * max(1, len(dims)))(*dims)
+    n = ctypes.c_size_t(12345)
+    st = msa.lib().msa_workspace_size(op, arr, len(dims), ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size_by_operation_matches_the_per_operation_calls():
+    lib = msa.lib()
+    n = ctypes.c_size_t(0)
+    bf = L.MSA_BF16
+    cases = [
+        (L.MSA_OP_ROUTE_SCORES, [1, 2048, 8, 128, 2048, 8, bf], lambda: lib.msa_route_scores_workspace(
+            1, 2048, 8, 128, 2048, 8, bf, ctypes.byref(n))),
+        (L.MSA_OP_ROUTE_SCORES, [4, 512, 8, 128, 195313, 8, bf], lambda: lib.msa_route_scores_workspace(
+            4, 512, 8, 128, 195313, 8, bf, ctypes.byref(n))),
+        (L.MSA_OP_TOPK_DOCS, [4, 195313, 16], lambda: lib.msa_topk_docs_workspace(4, 195313, 16, ctypes.byref(n))),
+        (L.MSA_OP_TOPK_DOCS_EXCLUDING, [2, 9000, 32], lambda: lib.msa_topk_docs_workspace(2, 9000, 32,
+                                                                                         ctypes.byref(n))),
+        (L.MSA_OP_ROUTE_ROUNDS, [3, 1, 2048, 8, 128, 2048, 8, 16, bf], lambda: lib.msa_route_rounds_workspace(
+            3, 1, 2048, 8, 128, 2048, 8, 16, bf, ctypes.byref(n))),
+        (L.MSA_OP_SPARSE_ATTN, [32, 1, 32, 8, 128, 128, 4096, bf], lambda: lib.msa_sparse_attn_workspace(
+            32, 1, 32, 8, 128, 128, 4096, bf, ctypes.byref(n))),
+        (L.MSA_OP_SPARSE_ATTN, [1, 2048, 32, 8, 128, 128, 2048, bf], lambda: lib.msa_sparse_attn_workspace(
+            1, 2048, 32, 8, 128, 128, 2048, bf, ctypes.byref(n))),
+        (L.MSA_OP_SPARSE_ATTN_BACKWARD, [1, 2048, 32, 8, 128, 128, 2048, bf],
+         lambda: lib.msa_sparse_attn_backward_workspace(1, 2048, 32, 8, 128, 128, 2048, bf, ctypes.byref(n))),
+    ]
+    for op, dims, per_op in cases:
+        assert per_op() == L.MSA_OK
+        st, got = _ws(op, dims)
+        assert st == L.MSA_OK and got == n.value, (op, dims, got, n.value)
+    # the tiled routing and the backward need scratch at these sizes
+    assert _ws(L.MSA_OP_ROUTE_SCORES, [1, 2048, 8, 128, 2048, 8, bf])[1] > 0
+    assert _ws(L.MSA_OP_SPARSE_ATTN_BACKWARD, [1, 2048, 32, 8, 128, 128, 2048, bf])[1] > 0
+    # operations without scratch
+    for op in (L.MSA_OP_POOL_CHUNKS, L.MSA_OP_GATHER_KV, L.MSA_OP_ENCODE_DOCS, L.MSA_OP_GDN_STATE_SUM,
+               L.MSA_OP_GATED_DELTA_RULE):
+        assert _ws(op, []) == (L.MSA_OK, 0)
+    # a wrong count of dims, an unknown op, an argument the operation rejects, an int32 overflow
+    assert _ws(L.MSA_OP_TOPK_DOCS, [4, 100])[0] == L.MSA_ERR_INVALID
+    assert "3 dims" in _err()
+    assert _ws(99, [1])[0] == L.MSA_ERR_INVALID
+    assert "unknown operation" in _err()
+    assert _ws(L.MSA_OP_TOPK_DOCS, [1, 100, 101])[0] == L.MSA_ERR_INVALID
+    assert _ws(L.MSA_OP_SPARSE_ATTN, [1 << 31, 1, 32, 8, 128, 0, 1, bf])[0] == L.MSA_ERR_INVALID
+    assert "int32" in _err()
+    # n_docs is a 64-bit argument and may exceed the int32 range on the way in (then rejected by the op)
+    assert _ws(L.MSA_OP_TOPK_DOCS, [1, 1 << 31, 16])[0] == L.MSA_ERR_INVALID
+    assert "2^31" in _err()
+    assert msa.msa_workspace_size(L.MSA_OP_TOPK_DOCS, [4, 195313, 16]) == 2 * 4 * 48 * 16 * 8
+
+
 def test_gather_validation():
     lib = msa.lib()
     p = ctypes.c_void_p(256)

@@ -139,3 +139,99 @@ def test_host_tier_rejects_pageable_memory():
     ids = torch.zeros((1, 2), dtype=torch.int32, device=DEV)
     with pytest.raises(ValueError, match="pinned"):
         msa.msa_gather_kv(kb, kb, ids, 8)
+
+
+def test_host_tier_memcpy_waits_only_for_its_own_stream():
+    """The per-document copies of the host tier while a routing launch runs on
+    another stream (queued before the call, so the host's wait for the ids
+    overlaps it) and another is queued on the same stream behind the copies:
+    the fetched rows equal the device gather, and both routings are intact."""
+    case("gather host tier memcpy overlapped with routing")
+    n_docs, cpd = 4096, 8
+    kb, vb = _bank(n_docs, cpd, 8, 128, torch.bfloat16, 21)
+    hk, hv = kb.cpu().pin_memory(), vb.cpu().pin_memory()
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    kr = torch.randn((n_docs * cpd, 8, 128), generator=g, device=DEV).to(torch.bfloat16)
+    norm = torch.linalg.vector_norm(kr.float(), dim=-1).contiguous()
+    q_small = torch.randn((4, 1, 8, 128), generator=g, device=DEV).to(torch.bfloat16)
+    q_big = torch.randn((4, 512, 8, 128), generator=g, device=DEV).to(torch.bfloat16)
+    ref_big = msa.msa_route_scores(q_big, kr, norm, cpd)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(a):
+        sc = msa.msa_route_scores(q_small, kr, norm, cpd)
+        ids, _ = msa.msa_topk_docs(sc, 16)
+    with torch.cuda.stream(b):                       # queued before the host-tier call
+        big = msa.msa_route_scores(q_big, kr, norm, cpd)
+        done_b = torch.cuda.Event()
+        done_b.record(b)
+    with torch.cuda.stream(a):
+        tk, tv = msa.msa_gather_kv(hk, hv, ids, cpd, host_memcpy=True)
+        b_running = not done_b.query()               # reported, not asserted: timing dependent
+        after = msa.msa_route_scores(q_big, kr, norm, cpd)     # queued behind the copies
+    torch.cuda.synchronize()
+    print(f"  the other stream's routing was {'still running' if b_running else 'done'} when the call returned")
+    dk, dv = msa.msa_gather_kv(kb, vb, ids, cpd)
+    torch.cuda.synchronize()
+    assert torch.equal(dk, tk) and torch.equal(dv, tv)
+    assert torch.equal(big, ref_big) and torch.equal(after, ref_big)
+
+
+def test_checked_gathers_in_threads_report_their_own_ids():
+    """Checked gathers from several threads at once, each on its own stream,
+    some with an out-of-range id: each call reports exactly its own result."""
+    import threading
+    case("checked gathers from 8 threads")
+    kb, vb = _bank(64, 8, 8, 128, torch.bfloat16, 4)
+    results = {}
+
+    def worker(i):
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            bad = i % 2 == 1
+            ids = torch.tensor([[1, 64 if bad else 2, 3]], dtype=torch.int32, device=DEV)
+            out = []
+            for _ in range(20):
+                try:
+                    msa.msa_gather_kv(kb, vb, ids, 8, checked=True)
+                    out.append(False)
+                except msa.MsaError:
+                    out.append(True)
+            results[i] = (bad, out)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    for i, (bad, out) in results.items():
+        assert out == [bad] * 20, (i, out)
+
+
+def test_binding_checks_output_shapes():
+    """Caller-supplied outputs of the wrong shape are refused before any launch."""
+    case("binding output shape checks")
+    kb, vb = _bank(16, 8, 8, 128, torch.bfloat16, 1)
+    ids = torch.tensor([[1, 2]], dtype=torch.int32, device=DEV)
+    small = torch.empty((1, 8, 8, 128), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError, match="k_sel"):
+        msa.msa_gather_kv(kb, vb, ids, 8, k_sel=small)
+    with pytest.raises(ValueError, match="whole number"):
+        msa.msa_gather_kv(kb[:100], vb[:100], ids, 8)
+    scores = torch.randn((2, 16), device=DEV)
+    with pytest.raises(ValueError, match="topk_ids"):
+        msa.msa_topk_docs(scores, 4, topk_ids=torch.empty((2, 3), dtype=torch.int32, device=DEV))
+    with pytest.raises(ValueError, match="topk_scores"):
+        msa.msa_topk_docs(scores, 4, topk_scores=torch.empty((1, 4), device=DEV))
+    q_r = torch.randn((2, 4, 8, 128), device=DEV).to(torch.bfloat16)
+    norm = torch.linalg.vector_norm(kb.float(), dim=-1).contiguous()
+    with pytest.raises(ValueError, match="doc_scores"):
+        msa.msa_route_scores(q_r, kb, norm, 8, doc_scores=torch.empty((2, 15), device=DEV))
+    q = torch.randn((1, 4, 8, 128), device=DEV).to(torch.bfloat16)
+    kl = torch.randn((1, 4, 2, 128), device=DEV).to(torch.bfloat16)
+    with pytest.raises(ValueError, match="out"):
+        msa.msa_sparse_attn(q, None, None, kl, kl, out=torch.empty((1, 3, 8, 128), dtype=torch.bfloat16,
+                                                                   device=DEV))
+    with pytest.raises(ValueError, match="lse"):
+        msa.msa_sparse_attn(q, None, None, kl, kl, lse=torch.empty((1, 8, 3), device=DEV))
