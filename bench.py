@@ -1272,7 +1272,7 @@ def route_scan_warm_cold(step, cfg, reps):
     sink = torch.empty((), dtype=torch.float32, device=step.kbar_r.device)
     w = work_route(cfg)
     out = {}
-    for name, before in (("warm", None), ("cold", lambda: torch.sum(flush, out=sink))):
+    for name, before in (("warm", None), ("cold", lambda: sink.copy_(flush.sum()))):
         fn()
         ms = time_launches(fn, max(reps, 10), before)
         e = roofline_entry(dict(w, bound="hbm"), ms)
