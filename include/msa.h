@@ -184,6 +184,25 @@ msa_status msa_route_scores(const void* q_r, const void* kbar_r, const float* kb
                             float* doc_scores, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * msa_route_scores without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc.  Same arguments, same result, same kernels
+ * as msa_route_scores; the scratch the tiled path needs (inverse query norms
+ * and per-block maxima, msa_route_scores_workspace() bytes) comes from a
+ * library-resident device array of 32 MiB per device, which each device the
+ * library runs on holds until the process ends.  The call allocates nothing.
+ * A call needing more scratch than that returns MSA_ERR_INVALID before any
+ * launch (e.g. 4 x 512 router tokens against 195,313 documents needs 50 MB).
+ * Every call on one device shares that array: calls that overlap in time on
+ * one device (on different streams, or from several threads) race on it and
+ * give undefined scores; serialise them (one stream per device suffices).
+ * Each call overwrites every byte it later reads, so nothing needs clearing.
+ * ---------------------------------------------------------------------- */
+msa_status msa_route_scores_noalloc(const void* q_r, const void* kbar_r, const float* kbar_r_norm,
+                                    int32_t batch, int32_t q_len, int32_t heads, int32_t dim, int64_t n_docs,
+                                    int32_t chunks_per_doc, msa_dtype dt, float* doc_scores, void* stream);
+
+/* ------------------------------------------------------------------------
  * S3  Top-k documents (MSA README "Overall Design" and "Inference Pipeline",
  *     stage 2: pick the top-k documents by routing score).
  *

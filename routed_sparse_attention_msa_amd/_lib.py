@@ -39,6 +39,8 @@ SIGNATURES = {
                                              c_int, POINTER(c_size_t)]),
     "msa_route_scores": (_STATUS, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
                                    c_int64, c_int32, c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "msa_route_scores_noalloc": (_STATUS, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
+                                           c_int64, c_int32, c_int, c_void_p, c_void_p]),
     "msa_topk_docs_workspace": (_STATUS, [c_int32, c_int64, c_int32, POINTER(c_size_t)]),
     "msa_topk_docs": (_STATUS, [c_void_p, c_int32, c_int64, c_int32, c_void_p, c_void_p, c_void_p,
                                 c_size_t, c_void_p]),

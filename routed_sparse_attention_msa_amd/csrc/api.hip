@@ -250,6 +250,28 @@ msa_status msa_route_scores(const void* q_r, const void* kbar_r, const float* kb
                     "msa_route_scores launch");
 }
 
+msa_status msa_route_scores_noalloc(const void* q_r, const void* kbar_r, const float* kbar_r_norm,
+                                    int32_t batch, int32_t q_len, int32_t heads, int32_t dim, int64_t n_docs,
+                                    int32_t chunks_per_doc, msa_dtype dt, float* doc_scores, void* stream) {
+  msa_status st = check_route(batch, q_len, heads, dim, n_docs, chunks_per_doc, dt);
+  if (st != MSA_OK) return st;
+  CHECK_ARG(q_r && kbar_r && kbar_r_norm && doc_scores, "null tensor pointer");
+  CHECK_ARG(aligned16(q_r) && aligned16(kbar_r) && aligned16(kbar_r_norm) && aligned16(doc_scores),
+            "tensors must be 16-byte aligned");
+  const size_t need = msa::route_workspace_bytes(batch, q_len, heads, dim, n_docs, chunks_per_doc, dt);
+  CHECK_ARG(need <= msa::kRouteStaticScratchBytes,
+            "this call needs %zu bytes of scratch, above the %zu bytes the library holds per device; use "
+            "msa_route_scores with a workspace", need, msa::kRouteStaticScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    hipError_t e = msa::route_static_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e, "routing scratch lookup");
+  }
+  return hip_status(msa::launch_route(q_r, kbar_r, kbar_r_norm, batch, q_len, heads, dim, n_docs,
+                                      chunks_per_doc, dt, doc_scores, ws, static_cast<hipStream_t>(stream)),
+                    "msa_route_scores_noalloc launch");
+}
+
 // ---------------------------------------------------------------------------
 static msa_status check_topk(int32_t batch, int64_t n_docs, int32_t k) {
   CHECK_ARG(batch > 0 && n_docs > 0, "sizes must be positive");

@@ -111,6 +111,11 @@ size_t route_workspace_bytes(int batch, int q_len, int heads, int dim, int64_t n
 hipError_t launch_route(const void* q_r, const void* kbar_r, const float* knorm, int batch,
                         int q_len, int heads, int dim, int64_t n_docs, int cpd, msa_dtype dt,
                         float* doc_scores, void* ws, hipStream_t s);
+// Device address of the library-resident routing scratch of the current
+// device (kRouteStaticScratchBytes, looked up once per device).
+constexpr size_t kRouteStaticScratchBytes = (size_t)32 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t route_static_scratch(void** ptr);
 
 size_t topk_workspace_bytes(int batch, int64_t n_docs, int k);
 hipError_t launch_topk(const float* scores, int batch, int64_t n_docs, int k, int32_t* ids,

@@ -39,6 +39,7 @@
 // All end with the max over each document's chunks (cross-lane shuffles)
 // and over the query tokens of each sequence.
 #include <algorithm>
+#include <mutex>
 
 #include "internal.h"
 
@@ -917,6 +918,32 @@ hipError_t launch_route(const void* q_r, const void* kbar_r, const float* knorm,
                        0, s, partial, q_len, batch, n_docs, doc_scores);
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Library-resident routing scratch, for callers that cannot allocate (code
+// under graph capture, serving loops that forbid hipMalloc).  Each device the
+// library runs on holds its own copy from the moment the module loads until
+// the process ends.  In host code `scratch` names a host-side stand-in, never
+// the device memory: its device address is looked up once per device with
+// hipGetSymbolAddress and only that address reaches a kernel.
+static __device__ __align__(256) uint8_t scratch[kRouteStaticScratchBytes];
+
+hipError_t route_static_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace msa
