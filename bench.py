@@ -103,6 +103,9 @@ def parse():
                    help="run a plain elementwise 1 GiB read + 1 GiB write five times and exit")
     p.add_argument("--summarize-stats", nargs=4, metavar=("STATS_CSV", "OUT_MD", "TITLE", "COMMAND"),
                    help="write a markdown summary of a rocprofv3 --stats kernel_stats.csv and exit")
+    p.add_argument("--summarize-counters", nargs="+", metavar="ARG",
+                   help="OUT_MD TITLE COMMANDS DIR [DIR ...]: per-kernel derived metrics (MFMA busy, VALU and LDS "
+                        "activity, bank conflicts, instruction mix) from rocprofv3 --pmc runs, then exit")
     p.add_argument("--summarize-traffic", metavar="DIR",
                    help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs under DIR into profiles/traffic.json")
     return p.parse_args()
@@ -315,6 +318,58 @@ def summarize_traffic(d):
     with open(os.path.join(ROOT, "profiles", "hbm-traffic_per-stage_all-workloads.md"), "w") as f:
         f.write("\n".join(md) + "\n")
     print(json.dumps(out, indent=1))
+
+
+N_XCD, N_CU = 8, 256      # MI355X: 8 XCDs, 256 CUs (4 SIMDs each)
+
+
+def summarize_counters(out_md, title, commands, dirs):
+    """Per-kernel medians of every counter in the rocprofv3 --pmc runs under
+    `dirs`, and the ratios read from them:
+      MFMA busy  = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs)
+      VALU, LDS, wait fractions = SQ_ACTIVE_INST_VALU, SQ_ACTIVE_INST_LDS, SQ_WAIT_INST_ANY
+                   over SQ_WAVE_CYCLES (per-wave shares of its lifetime)
+      bank-conflict share = SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS
+      VALU per MFMA = SQ_INSTS_VALU / SQ_INSTS_MFMA (SQ_INSTS_VALU counts the MFMAs too)."""
+    import csv
+    import glob
+    vals = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if "msa::" not in r["Kernel_Name"]:
+                        continue
+                    key = (_short_kernel(r["Kernel_Name"]), r["Counter_Name"])
+                    vals.setdefault(key, []).append(float(r["Counter_Value"]))
+    med = {k: _median(v) for k, v in vals.items()}
+    kernels = sorted({k for k, _ in med})
+    names = sorted({c for _, c in med})
+    g = lambda k, c: med.get((k, c))
+
+    def ratio(a, b, scale=1.0):
+        return None if a is None or not b else a / (b * scale)
+    lines = [f"# {title}", "", "Commands (repository root, one MI355X):", "", "```", *commands, "```", "",
+             "Derived (medians over dispatches): MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs "
+             "x 1024 SIMDs); VALU / LDS / wait = SQ_ACTIVE_INST_VALU, SQ_ACTIVE_INST_LDS, SQ_WAIT_INST_ANY over "
+             "SQ_WAVE_CYCLES; conflict = SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS; VALU/MFMA = SQ_INSTS_VALU / "
+             "SQ_INSTS_MFMA (SQ_INSTS_VALU includes the MFMAs).", "",
+             "| kernel | MFMA busy | VALU | LDS | wait | LDS conflict | VALU/MFMA |", "|---|---|---|---|---|---|---|"]
+    fmt = lambda x: "—" if x is None else f"{x:.3f}"
+    for k in kernels:
+        busy = ratio(g(k, "SQ_VALU_MFMA_BUSY_CYCLES"), g(k, "GRBM_GUI_ACTIVE"), 4 * N_CU / N_XCD)
+        wc = g(k, "SQ_WAVE_CYCLES")
+        lines.append(f"| `{k}` | {fmt(busy)} | {fmt(ratio(g(k, 'SQ_ACTIVE_INST_VALU'), wc))} | "
+                     f"{fmt(ratio(g(k, 'SQ_ACTIVE_INST_LDS'), wc))} | {fmt(ratio(g(k, 'SQ_WAIT_INST_ANY'), wc))} | "
+                     f"{fmt(ratio(g(k, 'SQ_LDS_BANK_CONFLICT'), g(k, 'SQ_ACTIVE_INST_LDS')))} | "
+                     f"{fmt(ratio(g(k, 'SQ_INSTS_VALU'), g(k, 'SQ_INSTS_MFMA')))} |")
+    lines += ["", "Raw medians per dispatch:", "", "| kernel | " + " | ".join(names) + " |",
+              "|---|" + "---|" * len(names)]
+    for k in kernels:
+        lines.append(f"| `{k}` | " + " | ".join("—" if g(k, c) is None else f"{g(k, c):.4g}" for c in names) + " |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def summarize_stats(csv_path, out_md, title, command):
@@ -1428,6 +1483,10 @@ def main():
         return
     if args.summarize_traffic:
         summarize_traffic(args.summarize_traffic)
+        return
+    if args.summarize_counters:
+        a = args.summarize_counters
+        summarize_counters(a[0], a[1], a[2].split(" ;; "), a[3:])
         return
     if args.copy_probe:
         copy_probe()

@@ -540,6 +540,7 @@ struct TiledSmem {
   uint8_t k[2][kNB * kStageK * 2];
   float rq[kMaxHeads + 1][kTB];      // rq[h]: scale applied before head h (h = H: final)
   float rk[kMaxHeads + 1][kNB];
+  float red[8][kNB];                 // epilogue: per row block, per document of the tile
 };
 
 // 16 B segment seg of a 128 B row, XOR-swizzled by (row / 2) % 8.  A 256 B
@@ -553,61 +554,92 @@ __device__ __forceinline__ int swz(int row, int seg) { return row * 128 + ((seg 
 __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
     const uint16_t* __restrict__ q_r, const uint16_t* __restrict__ kbar,
     const float* __restrict__ knorm, const float* __restrict__ iq, int t_tot, int t_len, int heads,
-    int64_t n_ch, int64_t n_docs, int cpd, int direct, int row_groups, float* __restrict__ partial,
-    float* __restrict__ out) {
+    int64_t n_ch, int64_t n_docs, int cpd, int direct, int row_groups, int n_tiles,
+    float* __restrict__ partial, float* __restrict__ out) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   TiledSmem& sm = *reinterpret_cast<TiledSmem*>(smem_raw);
-  float* red = reinterpret_cast<float*>(sm.q[0]);  // reused after the main loop: [8][kNB]
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int cl = lane & 31, hf = lane >> 5;
   const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves
-  // Workgroup order.  Workgroups go to the 8 XCDs round-robin by launch
-  // index, so XCD c runs indices c, c + 8, ...; they are given one
-  // contiguous run of a tile order in which the row tiles are split into
-  // row_groups contiguous groups, each enumerated column by column with its
-  // row tiles fastest.  An XCD's run then stays inside one row group: it
-  // reads each of its column tiles of the bank into its L2 once, for all of
-  // that group's row tiles, and keeps only the group's queries resident.
-  // The bank is read row_groups times, the queries about 8 / row_groups
-  // times.  (Column tiles fastest streamed the whole bank from HBM once per
-  // row tile.)  Any order is correct; this one only places reuse.
+  // Tile order.  Launch index v runs on XCD v % 8 (workgroups reach the XCDs
+  // round-robin); XCD c is given one contiguous run of a tile order in which
+  // the row tiles are split into row_groups contiguous groups, each
+  // enumerated column by column with its row tiles fastest.  An XCD's run
+  // then stays inside one row group: it reads each of its column tiles of the
+  // bank into its L2 once, for all of that group's row tiles, and keeps only
+  // the group's queries resident.  The bank is read row_groups times, the
+  // queries about 8 / row_groups times.  (Column tiles fastest streamed the
+  // whole bank from HBM once per row tile.)  Any order is correct; this one
+  // only places reuse.  The kernel is persistent: workgroup w takes the
+  // virtual launch indices w, w + G, w + 2G, ... (G = gridDim.x, a multiple
+  // of 8 when smaller than the tile count, so they stay on w's XCD).
   const int n_ty = (t_tot + kTB - 1) / kTB;
-  const unsigned n_tx = gridDim.x / (unsigned)n_ty;
-  const unsigned n_wg = gridDim.x, xcd = blockIdx.x % 8u, per = n_wg / 8u, extra = n_wg % 8u;
-  const unsigned tile = xcd * per + min(xcd, extra) + blockIdx.x / 8u;
-  int grp = 0;
-  while (grp + 1 < row_groups && n_tx * (unsigned)((grp + 1) * n_ty / row_groups) <= tile) ++grp;
-  const int r_lo = grp * n_ty / row_groups, r_hi = (grp + 1) * n_ty / row_groups;
-  const unsigned in_grp = tile - n_tx * (unsigned)r_lo;
-  const int ty = r_lo + (int)(in_grp % (unsigned)(r_hi - r_lo));
-  const int64_t tx = in_grp / (unsigned)(r_hi - r_lo);
-  const int row0 = ty * kTB;
-  const int64_t col0 = tx * kNB;
+  const unsigned n_tx = (unsigned)n_tiles / (unsigned)n_ty;
+  auto tile_at = [&](unsigned v, int* ty_out, int64_t* tx_out) {
+    const unsigned xcd = v % 8u, per = (unsigned)n_tiles / 8u, extra = (unsigned)n_tiles % 8u;
+    const unsigned tile = xcd * per + min(xcd, extra) + v / 8u;
+    int grp = 0;
+    while (grp + 1 < row_groups && n_tx * (unsigned)((grp + 1) * n_ty / row_groups) <= tile) ++grp;
+    const int r_lo = grp * n_ty / row_groups, r_hi = (grp + 1) * n_ty / row_groups;
+    const unsigned in_grp = tile - n_tx * (unsigned)r_lo;
+    *ty_out = r_lo + (int)(in_grp % (unsigned)(r_hi - r_lo));
+    *tx_out = in_grp / (unsigned)(r_hi - r_lo);
+  };
   const size_t row_elems = (size_t)heads * kDim;
+  const uint32_t row_bytes = (uint32_t)(row_elems * 2);
+  const unsigned G = gridDim.x;
 
   // --- per-head scale tables -------------------------------------------------
-  for (int idx = tid; idx < kTB; idx += kTiledThreads) {
-    const int r = row0 + idx;
-    float prev = 0.f;
-    for (int h = 0; h < heads; ++h) {
-      const float cur = r < t_tot ? iq[(size_t)r * heads + h] : 1.f;
-      if (h > 0) sm.rq[h][idx] = prev / cur;
-      prev = cur;
+  // Threads 0..255 own the tile's rows (inverse query norms), 256..511 its
+  // columns (inverse key norms); every head's value is loaded at once, early
+  // (for the next tile: during the current tile's last head), and turned into
+  // the chained ratios when the tables are free.
+  float tv[kMaxHeads];
+  // (head indices past `heads` reread the last head, so the loads need no
+  // per-head predicate and stay inside the row)
+  auto load_tables = [&](int row0, int64_t col0) {
+    if (tid < kTB) {
+      const int r = row0 + tid;
+      const bool ok = r < t_tot;
+      const float* src = iq + (size_t)(ok ? r : 0) * heads;
+#pragma unroll
+      for (int h = 0; h < kMaxHeads; ++h) tv[h] = src[min(h, heads - 1)];
+#pragma unroll
+      for (int h = 0; h < kMaxHeads; ++h) tv[h] = ok ? tv[h] : 1.f;
+    } else {
+      const int64_t n = col0 + (tid - kTB);
+      const bool ok = n < n_ch;
+      const float* src = knorm + (ok ? n : 0) * heads;
+#pragma unroll
+      for (int h = 0; h < kMaxHeads; ++h) tv[h] = src[min(h, heads - 1)];
+#pragma unroll
+      for (int h = 0; h < kMaxHeads; ++h) tv[h] = ok ? 1.f / fmaxf(tv[h], kEps) : 0.f;
     }
-    sm.rq[heads][idx] = prev;
-  }
-  for (int idx = tid; idx < kNB; idx += kTiledThreads) {
-    const int64_t n = col0 + idx;
-    float prev = 0.f;
-    for (int h = 0; h < heads; ++h) {
-      const float cur = n < n_ch ? 1.f / fmaxf(knorm[n * heads + h], kEps) : 0.f;
-      if (h > 0) sm.rk[h][idx] = cur != 0.f ? prev / cur : 0.f;
-      prev = cur;
+  };
+  auto store_tables = [&] {
+    if (tid < kTB) {
+#pragma unroll
+      for (int h = 1; h < kMaxHeads; ++h)
+        if (h < heads) sm.rq[h][tid] = tv[h - 1] / tv[h];
+      float last = tv[0];
+#pragma unroll
+      for (int h = 1; h < kMaxHeads; ++h)
+        if (h < heads) last = tv[h];
+      sm.rq[heads][tid] = last;
+    } else {
+      const int c = tid - kTB;
+#pragma unroll
+      for (int h = 1; h < kMaxHeads; ++h)
+        if (h < heads) sm.rk[h][c] = tv[h] != 0.f ? tv[h - 1] / tv[h] : 0.f;
+      float last = tv[0];
+#pragma unroll
+      for (int h = 1; h < kMaxHeads; ++h)
+        if (h < heads) last = tv[h];
+      sm.rk[heads][c] = last / (float)heads;
     }
-    sm.rk[heads][idx] = prev / (float)heads;
-  }
+  };
 
   // --- staging: 4 x 16 B of q and 4 x 16 B of k per thread per stage ----------
   // Buffer loads: a per-lane offset fixed for the kernel plus the stage's
@@ -615,7 +647,6 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
   // and read as zeros, so the loads carry no branches and no address math.
   // (Base and size pass through readfirstlane: the compiler did not prove
   // them uniform and wrapped every load in a loop over the lanes' values.)
-  const uint32_t row_bytes = (uint32_t)(row_elems * 2);
   auto uniform_rsrc = [](const uint16_t* p, size_t bytes) {
     const uint64_t a = (uint64_t)(uintptr_t)p;
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
@@ -623,23 +654,42 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
     void* u = reinterpret_cast<void*>((uintptr_t)(((uint64_t)hi << 32) | lo));
     return __builtin_amdgcn_make_buffer_rsrc(u, 0, (int)__builtin_amdgcn_readfirstlane((uint32_t)bytes), 0x00020000);
   };
-  const __amdgpu_buffer_rsrc_t qrs =
-      uniform_rsrc(q_r + (size_t)row0 * row_elems, (size_t)max(0, min(kTB, t_tot - row0)) * row_bytes);
-  const __amdgpu_buffer_rsrc_t krs =
-      uniform_rsrc(kbar + (size_t)col0 * row_elems, (size_t)max<int64_t>(0, min<int64_t>(kNB, n_ch - col0)) * row_bytes);
+  auto q_rsrc = [&](int row0) {
+    return uniform_rsrc(q_r + (size_t)row0 * row_elems, (size_t)max(0, min(kTB, t_tot - row0)) * row_bytes);
+  };
+  auto k_rsrc = [&](int64_t col0) {
+    return uniform_rsrc(kbar + (size_t)col0 * row_elems,
+                        (size_t)max<int64_t>(0, min<int64_t>(kNB, n_ch - col0)) * row_bytes);
+  };
   uint32_t voff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = tid + kTiledThreads * i;
     voff[i] = (uint32_t)(c >> 3) * row_bytes + (c & 7) * 16;
   }
+
+  // first tile of this workgroup: its tables, stage 0 in buffer 0, stage 1 in registers
+  unsigned v = blockIdx.x;
+  int ty;
+  int64_t tx;
+  tile_at(v, &ty, &tx);
+  // the tile the staging loads read: the current one, switched to the next
+  // tile for the current tile's last head (whose loads are the next tile's
+  // first two stages)
+  __amdgpu_buffer_rsrc_t ld_q = q_rsrc(ty * kTB), ld_k = k_rsrc(tx * kNB);
+  int ty_n = ty;
+  int64_t tx_n = tx;
+  bool has_next = false;
+  const int n_stages = 2 * heads;
   u32x4 pq[4], pk[4];
-  // one of the four 16 B pieces of q and of k per thread: load for a stage,
-  // store to an LDS buffer
+  // one of the four 16 B pieces of q and of k per thread: load for a stage
+  // (stages n_stages and n_stages + 1 are the next tile's first two), store
+  // to an LDS buffer
   auto gload1 = [&](int stage, int i) {
-    const uint32_t soff = (uint32_t)((stage >> 1) * kDim + (stage & 1) * 64) * 2;
-    pq[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, voff[i], soff, 0));
-    pk[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, voff[i], soff, 0));
+    const int st = stage >= n_stages ? stage - n_stages : stage;
+    const uint32_t soff = (uint32_t)((st >> 1) * kDim + (st & 1) * 64) * 2;
+    pq[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ld_q, voff[i], soff, 0));
+    pk[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ld_k, voff[i], soff, 0));
   };
   auto lstore1 = [&](int buf, int i) {
     const int c = tid + kTiledThreads * i;
@@ -647,13 +697,17 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
     *reinterpret_cast<u32x4*>(&sm.q[buf][swz(r, seg)]) = pq[i];
     *reinterpret_cast<u32x4*>(&sm.k[buf][swz(r, seg)]) = pk[i];
   };
+  load_tables(ty * kTB, tx * kNB);
+  store_tables();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) gload1(0, i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lstore1(0, i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) gload1(1, i);
+  __syncthreads();
 
   f32x16 acc[4][2];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
-
   // chain to head hn (or, with hn == heads, apply the final scale); the four
   // factor reads of a row block are issued together, so their LDS latencies
   // overlap.
@@ -712,58 +766,79 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
     }
   };
 
-  // Two stages (the halves of one head) per iteration; the chained rescale
-  // to the next head closes it.  Loads are issued unconditionally (clamped to
-  // the last stage) so one fixed set is in flight.
-  const int n_stages = 2 * heads;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) gload1(0, i);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) lstore1(0, i);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) gload1(1, i);
-  __syncthreads();
-  for (int h = 0; h < heads; ++h) {
-    stage_mfma(0, 1, min(2 * h + 2, n_stages - 1));
-    __syncthreads();
-    stage_mfma(1, 0, min(2 * h + 3, n_stages - 1));
-    rescale(h + 1);                     // h + 1 == heads: the final scale
-    __syncthreads();
-  }
-
-  // --- epilogue: max over each row block's 32 rows, then each doc's chunks ----
   const int ndw = kNB / cpd;  // documents per workgroup tile
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      float m = acc[a][b][0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) m = fmaxf(m, acc[a][b][i]);
-      m = fmaxf(m, __shfl_xor(m, 32));
-      m = doc_max(m, cpd);
-      const int c = wn * 64 + b * 32 + cl;
-      if (hf == 0 && (cl % cpd) == 0) red[(wm * 4 + a) * ndw + c / cpd] = m;
-    }
-  }
-  __syncthreads();
   const int n_blk = t_tot / 32;
-  for (int idx = tid; idx < 8 * ndw; idx += kTiledThreads) {
-    const int rb = idx / ndw, dw = idx - rb * ndw;
-    const int gblk = ty * 8 + rb;
-    if (gblk >= n_blk) continue;
-    const int b = gblk * 32 / t_len;
-    const bool start = rb == 0 || ((gblk - 1) * 32 / t_len) != b;
-    if (!start) continue;
-    float m = red[rb * ndw + dw];
-    for (int r2 = rb + 1; r2 < 8 && ty * 8 + r2 < n_blk && (ty * 8 + r2) * 32 / t_len == b; ++r2)
-      m = fmaxf(m, red[r2 * ndw + dw]);
-    const int64_t doc = col0 / cpd + dw;
-    if (doc >= n_docs) continue;
-    if (direct)
-      out[(size_t)b * n_docs + doc] = m;
-    else
-      partial[(size_t)gblk * n_docs + doc] = m;
+  while (true) {
+    const int row0 = ty * kTB;
+    const int64_t col0 = tx * kNB;
+    has_next = v + G < (unsigned)n_tiles;
+    if (has_next) tile_at(v + G, &ty_n, &tx_n);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+
+    // Two stages (the halves of one head) per iteration; the chained rescale
+    // to the next head closes it.  The last head's stages load the next
+    // tile's first two (or, on the last tile, a clamped copy), so its loop
+    // starts from LDS.
+    for (int h = 0; h < heads; ++h) {
+      const bool last = h == heads - 1;
+      if (last && has_next) {
+        ld_q = q_rsrc(ty_n * kTB);
+        ld_k = k_rsrc(tx_n * kNB);
+      }
+      // on the last tile the last head's loads are clamped copies of its last stage
+      const int clamp = last && !has_next ? n_stages - 1 : 1 << 30;
+      stage_mfma(0, 1, min(2 * h + 2, clamp));
+      __syncthreads();
+      stage_mfma(1, 0, min(2 * h + 3, last ? clamp : n_stages - 1));
+      rescale(h + 1);                   // h + 1 == heads: the final scale
+      __syncthreads();
+    }
+    // The next tile's scale factors are loaded now and go into the tables
+    // (every wave is past its last read of them) behind the block maxima.
+    if (has_next) load_tables(ty_n * kTB, tx_n * kNB);
+
+    // --- epilogue: max over each row block's 32 rows, then each doc's chunks --
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        float m = acc[a][b][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) m = fmaxf(m, acc[a][b][i]);
+        m = fmaxf(m, __shfl_xor(m, 32));
+        m = doc_max(m, cpd);
+        const int c = wn * 64 + b * 32 + cl;
+        if (hf == 0 && (cl % cpd) == 0) sm.red[wm * 4 + a][c / cpd] = m;
+      }
+    }
+    if (has_next) store_tables();
+    __syncthreads();
+    for (int idx = tid; idx < 8 * ndw; idx += kTiledThreads) {
+      const int rb = idx / ndw, dw = idx - rb * ndw;
+      const int gblk = ty * 8 + rb;
+      if (gblk >= n_blk) continue;
+      const int b = gblk * 32 / t_len;
+      const bool start = rb == 0 || ((gblk - 1) * 32 / t_len) != b;
+      if (!start) continue;
+      float m = sm.red[rb][dw];
+      for (int r2 = rb + 1; r2 < 8 && ty * 8 + r2 < n_blk && (ty * 8 + r2) * 32 / t_len == b; ++r2)
+        m = fmaxf(m, sm.red[r2][dw]);
+      const int64_t doc = col0 / cpd + dw;
+      if (doc >= n_docs) continue;
+      if (direct)
+        out[(size_t)b * n_docs + doc] = m;
+      else
+        partial[(size_t)gblk * n_docs + doc] = m;
+    }
+    (void)row0;
+    if (!has_next) break;
+    // (the next tile's epilogue writes red only after many barriers)
+    v += G;
+    ty = ty_n;
+    tx = tx_n;
   }
 }
 
@@ -897,7 +972,12 @@ hipError_t launch_route(const void* q_r, const void* kbar_r, const float* knorm,
   hipLaunchKernelGGL(route_qnorm_kernel, dim3((unsigned)((items * 16 + 255) / 256)), dim3(256), 0, s,
                      q, (int64_t)t_tot, heads, iq);
   const bool direct = tiled_direct(q_len);
-  const dim3 grid((unsigned)(((n_ch + kNB - 1) / kNB) * ((t_tot + kTB - 1) / kTB)));
+  const int64_t n_tiles = ((n_ch + kNB - 1) / kNB) * ((t_tot + kTB - 1) / kTB);
+  // persistent: one workgroup per CU (the LDS holds one), a multiple of 8 of
+  // them so each keeps to its XCD's run of tiles
+  const int n_cu = device_cu_count();
+  const int64_t wgs = n_tiles <= n_cu ? n_tiles : std::max<int64_t>(8, (n_cu / 8) * 8);
+  const dim3 grid((unsigned)wgs);
   const size_t smem = sizeof(TiledSmem);
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(route_tiled_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -912,7 +992,8 @@ hipError_t launch_route(const void* q_r, const void* kbar_r, const float* knorm,
          (size_t)t_tot * heads * kDim * 2 > (size_t)row_groups * (2u << 20))
     row_groups *= 2;
   hipLaunchKernelGGL(route_tiled_kernel, grid, dim3(kTiledThreads), smem, s, q, k, knorm, iq, t_tot,
-                     q_len, heads, n_ch, n_docs, cpd, direct ? 1 : 0, row_groups, partial, doc_scores);
+                     q_len, heads, n_ch, n_docs, cpd, direct ? 1 : 0, row_groups, (int)n_tiles, partial,
+                     doc_scores);
   if (!direct) {
     hipLaunchKernelGGL(route_combine_kernel, dim3((unsigned)((n_docs + 255) / 256), batch), dim3(256),
                        0, s, partial, q_len, batch, n_docs, doc_scores);

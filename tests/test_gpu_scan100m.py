@@ -9,7 +9,7 @@ documents are fetched.
 Parity, stage by stage on the GPU's own intermediates:
   * routing scores of sampled documents (and of every selected one) against
     the oracle on those documents' chunks;
-  * for sequences 0 and 1, the oracle streamed over the whole bank, and the
+  * for every sequence, the oracle streamed over the whole bank, and the
     GPU's top-16 checked by the band rule against it (this bank sits in the
     near-tie regime: many documents within 1e-4 of the 16th score), with the
     exact-match rate reported;
@@ -114,7 +114,7 @@ def test_route_sampled(bank, routed):
     assert err <= 2e-5          # products of bf16 values are exact in float32
 
 
-@pytest.mark.parametrize("b", [0, 1])
+@pytest.mark.parametrize("b", [0, 1, 2, 3])
 def test_topk_band_over_whole_bank(bank, routed, b):
     kbar_r, _, q_r = bank
     scores, ids, top = routed
