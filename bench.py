@@ -98,6 +98,8 @@ def parse():
                    default="prefill")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--step-only", action="store_true",
+                   help="time the step alone: no routing sweep, host-tier or warm/cold extras (for profiling)")
     # profiling helpers (see "Profiles" in the module docstring)
     p.add_argument("--copy-probe", action="store_true",
                    help="run a plain elementwise 1 GiB read + 1 GiB write five times and exit")
@@ -287,8 +289,9 @@ def summarize_traffic(d):
            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/copy_fetch -o run -- python3 bench.py --copy-probe",
            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/copy_write -o run -- python3 bench.py --copy-probe"]
     for wl in STAGE_KERNELS:
+        extra = " --step-only" if wl == "scan100m" else ""
         md += [f"rocprofv3 --pmc {c} --output-format csv -d DIR/{wl}_{c.split('_')[0].lower()} -o run -- "
-               f"python3 bench.py --workload {wl} --steps 2 --warmup 1 --no-cpu-baseline"
+               f"python3 bench.py --workload {wl} --steps 2 --warmup 1 --no-cpu-baseline{extra}"
                for c in ("FETCH_SIZE", "WRITE_SIZE")]
     md += ["python bench.py --summarize-traffic DIR", "```", "",
            f"Calibration: a 1 GiB elementwise read+write reads {copy['fetch']:.0f} KiB (FETCH_SIZE) and writes "
@@ -1105,10 +1108,12 @@ def main_scan(args):
     roof = {k: stages[dom][k] for k in ("bound", "achieved", "peak", "unit", "frac")}
     roof.update({"kernel": dom, "avg_launch_ms": stages[dom]["avg_launch_ms"],
                  "traffic": measured_traffic("scan100m", dom)})
-    print("[bench] routing sweep over the 3.2 GB bank", file=sys.stderr, flush=True)
-    sweep = step.sweep(max(5, min(args.steps, 20)))
-    print("[bench] host-tier fetch, alone and overlapped", file=sys.stderr, flush=True)
-    host = step.host_tier(max(5, min(args.steps, 20)))
+    sweep = host = None
+    if not args.step_only:
+        print("[bench] routing sweep over the 3.2 GB bank", file=sys.stderr, flush=True)
+        sweep = step.sweep(max(5, min(args.steps, 20)))
+        print("[bench] host-tier fetch, alone and overlapped", file=sys.stderr, flush=True)
+        host = step.host_tier(max(5, min(args.steps, 20)))
     c = step.cfg
     rec = {
         "metric": "query tokens/s of the routing scan at a 100M-token share (3.2 GB router bank) with the "
@@ -1579,7 +1584,7 @@ def main():
                         "encoded_tokens_per_s": cfg.n_doc * cfg.doc_len / (3 * avg / 1e3),
                         "pass": "pool K, pool V, pool K_r (+ norms): 2048 docs x 512 tokens each"})
     route_cold = None
-    if args.workload == "decode":
+    if args.workload == "decode" and not args.step_only:
         route_cold = route_scan_warm_cold(step, cfg, args.steps)
     rec = {
         "metric": ("query tokens/s at 1M-token memory (routing-scan GB/s + sparse-attn TFLOP/s in stages)"
