@@ -596,9 +596,11 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
   // columns (inverse key norms); every head's value is loaded at once, early
   // (for the next tile: during the current tile's last head), and turned into
   // the chained ratios when the tables are free.
-  float tv[kMaxHeads];
-  // (head indices past `heads` reread the last head, so the loads need no
-  // per-head predicate and stay inside the row)
+  // (Head indices past `heads` reread the last head, so the loads need no
+  // per-head predicate and stay inside the row.  The last head's value is
+  // loaded on its own: selecting tv[heads - 1] would index the array
+  // dynamically and move it to scratch memory.)
+  float tv[kMaxHeads], tv_last;
   auto load_tables = [&](int row0, int64_t col0) {
     if (tid < kTB) {
       const int r = row0 + tid;
@@ -606,16 +608,20 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
       const float* src = iq + (size_t)(ok ? r : 0) * heads;
 #pragma unroll
       for (int h = 0; h < kMaxHeads; ++h) tv[h] = src[min(h, heads - 1)];
+      tv_last = src[heads - 1];
 #pragma unroll
       for (int h = 0; h < kMaxHeads; ++h) tv[h] = ok ? tv[h] : 1.f;
+      tv_last = ok ? tv_last : 1.f;
     } else {
       const int64_t n = col0 + (tid - kTB);
       const bool ok = n < n_ch;
       const float* src = knorm + (ok ? n : 0) * heads;
 #pragma unroll
       for (int h = 0; h < kMaxHeads; ++h) tv[h] = src[min(h, heads - 1)];
+      tv_last = src[heads - 1];
 #pragma unroll
       for (int h = 0; h < kMaxHeads; ++h) tv[h] = ok ? 1.f / fmaxf(tv[h], kEps) : 0.f;
+      tv_last = ok ? 1.f / fmaxf(tv_last, kEps) : 0.f;
     }
   };
   auto store_tables = [&] {
@@ -623,21 +629,13 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
 #pragma unroll
       for (int h = 1; h < kMaxHeads; ++h)
         if (h < heads) sm.rq[h][tid] = tv[h - 1] / tv[h];
-      float last = tv[0];
-#pragma unroll
-      for (int h = 1; h < kMaxHeads; ++h)
-        if (h < heads) last = tv[h];
-      sm.rq[heads][tid] = last;
+      sm.rq[heads][tid] = tv_last;
     } else {
       const int c = tid - kTB;
 #pragma unroll
       for (int h = 1; h < kMaxHeads; ++h)
         if (h < heads) sm.rk[h][c] = tv[h] != 0.f ? tv[h - 1] / tv[h] : 0.f;
-      float last = tv[0];
-#pragma unroll
-      for (int h = 1; h < kMaxHeads; ++h)
-        if (h < heads) last = tv[h];
-      sm.rk[heads][c] = last / (float)heads;
+      sm.rk[heads][c] = tv_last / (float)heads;
     }
   };
 
