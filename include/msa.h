@@ -187,12 +187,13 @@ msa_status msa_route_scores(const void* q_r, const void* kbar_r, const float* kb
  * msa_route_scores without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, serving loops and
  * harnesses that forbid hipMalloc.  Same arguments, same result, same kernels
- * as msa_route_scores; the scratch the tiled path needs (inverse query norms
- * and per-block maxima, msa_route_scores_workspace() bytes) comes from a
- * library-resident device array of 32 MiB per device, which each device the
- * library runs on holds until the process ends.  The call allocates nothing.
- * A call needing more scratch than that returns MSA_ERR_INVALID before any
- * launch (e.g. 4 x 512 router tokens against 195,313 documents needs 50 MB).
+ * as msa_route_scores; the scratch the tiled path needs (the inverse query
+ * norms, msa_route_scores_workspace() bytes: 32 bytes per router token at 8
+ * heads) comes from a library-resident device array of 32 MiB per device,
+ * which each device the library runs on holds until the process ends.  The
+ * call allocates nothing.  A call needing more scratch than that (more than
+ * 1,048,576 router tokens at 8 heads) returns MSA_ERR_INVALID before any
+ * launch.
  * Every call on one device shares that array: calls that overlap in time on
  * one device (on different streams, or from several threads) race on it and
  * give undefined scores; serialise them (one stream per device suffices).

@@ -35,7 +35,10 @@
 //  * route_tiled   (many query rows): 256x256 output tile per workgroup,
 //    8 waves (2 x 4), each wave 128 rows x 64 columns (4 x 2 MFMA blocks);
 //    query and key slices are staged through XOR-swizzled, double-buffered
-//    LDS, 64 k-elements of one head per stage.  MFMA-bound.
+//    LDS, 64 k-elements of one head per stage; persistent workgroups.
+//    MFMA-bound.  A sequence longer than one 256-row tile gets its maximum
+//    over the tiles by atomic maxima into the scores (set to -inf by the
+//    query-norm kernel that runs first).
 // All end with the max over each document's chunks (cross-lane shuffles)
 // and over the query tokens of each sequence.
 #include <algorithm>
@@ -63,7 +66,12 @@ __device__ __forceinline__ int acc_row(int i, int hf) { return 8 * (i >> 2) + 4 
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void route_qnorm_kernel(const uint16_t* __restrict__ q_r,
                                                           int64_t rows, int heads,
-                                                          float* __restrict__ iq) {
+                                                          float* __restrict__ iq,
+                                                          float* __restrict__ fill, int64_t n_fill) {
+  // (With `fill`, also set fill[0 .. n_fill) to -inf: the scores that the
+  // tiled kernel then raises with atomic maxima.)
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_fill; i += (int64_t)gridDim.x * 256)
+    fill[i] = -INFINITY;
   // 16 lanes per (row, head): 16 lanes x 8 elements = 128.
   const int64_t item = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
   const int sub = threadIdx.x & 15;
@@ -83,6 +91,17 @@ __global__ __launch_bounds__(256) void route_qnorm_kernel(const uint16_t* __rest
 // ---------------------------------------------------------------------------
 // epilogue helpers
 // ---------------------------------------------------------------------------
+
+// Atomic maximum of float values through integer atomics (the scores start
+// at -inf): a non-negative value orders like its bits as a signed integer,
+// a negative one inversely to its bits as an unsigned integer, so the larger
+// float always wins.  The result does not depend on the order of the calls.
+__device__ __forceinline__ void atomic_max_float(float* p, float v) {
+  if (__float_as_int(v) >= 0)
+    atomicMax(reinterpret_cast<int*>(p), __float_as_int(v));
+  else
+    atomicMin(reinterpret_cast<unsigned int*>(p), __float_as_uint(v));
+}
 
 // Max over the C consecutive columns (lanes) of each document.
 __device__ __forceinline__ float doc_max(float v, int cpd) {
@@ -555,7 +574,7 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
     const uint16_t* __restrict__ q_r, const uint16_t* __restrict__ kbar,
     const float* __restrict__ knorm, const float* __restrict__ iq, int t_tot, int t_len, int heads,
     int64_t n_ch, int64_t n_docs, int cpd, int direct, int row_groups, int n_tiles,
-    float* __restrict__ partial, float* __restrict__ out) {
+    float* __restrict__ out) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   TiledSmem& sm = *reinterpret_cast<TiledSmem*>(smem_raw);
 
@@ -829,7 +848,7 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
       if (direct)
         out[(size_t)b * n_docs + doc] = m;
       else
-        partial[(size_t)gblk * n_docs + doc] = m;
+        atomic_max_float(out + (size_t)b * n_docs + doc, m);
     }
     (void)row0;
     if (!has_next) break;
@@ -838,21 +857,6 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
     ty = ty_n;
     tx = tx_n;
   }
-}
-
-// out[b][doc] = max over the partial rows written for sequence b: its first
-// 32-row block and every block that starts a 256-row tile.
-__global__ __launch_bounds__(256) void route_combine_kernel(const float* __restrict__ partial,
-                                                            int t_len, int batch, int64_t n_docs,
-                                                            float* __restrict__ out) {
-  const int64_t doc = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int b = blockIdx.y;
-  if (doc >= n_docs) return;
-  const int blk0 = b * t_len / 32, blk1 = (b + 1) * t_len / 32;
-  float m = -INFINITY;
-  for (int g = blk0; g < blk1; ++g)
-    if (g == blk0 || (g % 8) == 0) m = fmaxf(m, partial[(size_t)g * n_docs + doc]);
-  out[(size_t)b * n_docs + doc] = m;
 }
 
 enum class RoutePath { Generic, Scan, Stream, Tiled };
@@ -886,10 +890,7 @@ size_t route_workspace_bytes(int batch, int q_len, int heads, int dim, int64_t n
                              msa_dtype dt) {
   if (pick(batch, q_len, heads, dim, cpd, dt) != RoutePath::Tiled) return 0;
   const size_t t_tot = (size_t)batch * q_len;
-  size_t bytes = t_tot * heads * sizeof(float);  // inverse query norms
-  bytes = (bytes + 255) & ~(size_t)255;
-  if (!tiled_direct(q_len)) bytes += (t_tot / 32) * (size_t)n_docs * sizeof(float);
-  return bytes;
+  return t_tot * heads * sizeof(float);  // inverse query norms
 }
 
 hipError_t launch_route(const void* q_r, const void* kbar_r, const float* knorm, int batch,
@@ -962,14 +963,14 @@ hipError_t launch_route(const void* q_r, const void* kbar_r, const float* knorm,
 #undef MSA_STREAM
     return hipGetLastError();
   }
-  // tiled
+  // tiled: the inverse query norms (and, when a sequence spans several
+  // 256-row tiles, the scores set to -inf for the tiles' atomic maxima), then
+  // the tiled kernel
   float* iq = static_cast<float*>(ws);
-  size_t off = ((size_t)t_tot * heads * sizeof(float) + 255) & ~(size_t)255;
-  float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + off);
   const int64_t items = (int64_t)t_tot * heads;
-  hipLaunchKernelGGL(route_qnorm_kernel, dim3((unsigned)((items * 16 + 255) / 256)), dim3(256), 0, s,
-                     q, (int64_t)t_tot, heads, iq);
   const bool direct = tiled_direct(q_len);
+  hipLaunchKernelGGL(route_qnorm_kernel, dim3((unsigned)((items * 16 + 255) / 256)), dim3(256), 0, s,
+                     q, (int64_t)t_tot, heads, iq, doc_scores, direct ? (int64_t)0 : (int64_t)batch * n_docs);
   const int64_t n_tiles = ((n_ch + kNB - 1) / kNB) * ((t_tot + kTB - 1) / kTB);
   // persistent: one workgroup per CU (the LDS holds one), a multiple of 8 of
   // them so each keeps to its XCD's run of tiles
@@ -990,12 +991,7 @@ hipError_t launch_route(const void* q_r, const void* kbar_r, const float* knorm,
          (size_t)t_tot * heads * kDim * 2 > (size_t)row_groups * (2u << 20))
     row_groups *= 2;
   hipLaunchKernelGGL(route_tiled_kernel, grid, dim3(kTiledThreads), smem, s, q, k, knorm, iq, t_tot,
-                     q_len, heads, n_ch, n_docs, cpd, direct ? 1 : 0, row_groups, (int)n_tiles, partial,
-                     doc_scores);
-  if (!direct) {
-    hipLaunchKernelGGL(route_combine_kernel, dim3((unsigned)((n_docs + 255) / 256), batch), dim3(256),
-                       0, s, partial, q_len, batch, n_docs, doc_scores);
-  }
+                     q_len, heads, n_ch, n_docs, cpd, direct ? 1 : 0, row_groups, (int)n_tiles, doc_scores);
   return hipGetLastError();
 }
 

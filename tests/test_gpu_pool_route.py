@@ -120,8 +120,8 @@ def _route_case(batch, q_len, heads, dim, n_docs, cpd, dtype, seed, planted=None
     (1, 33, 8, 128, 40, 8, torch.bfloat16),       # odd query length
     (2, 16, 4, 64, 50, 4, torch.bfloat16),        # other head count / dim / chunks
     (1, 8, 3, 96, 20, 5, torch.bfloat16),         # shape-general path
-    # MFMA tiled path: direct and combined partials, ragged column tiles
-    (1, 512, 8, 128, 100, 8, torch.bfloat16),     # 2 row tiles per sequence, combine
+    # MFMA tiled path: direct, and sequences over several row tiles (atomic maxima), ragged column tiles
+    (1, 512, 8, 128, 100, 8, torch.bfloat16),     # 2 row tiles per sequence
     (3, 96, 8, 128, 70, 8, torch.bfloat16),       # sequences straddle 256-row tiles
     (5, 64, 8, 128, 33, 8, torch.bfloat16),       # several sequences per tile, direct
     (1, 2048, 8, 128, 300, 8, torch.bfloat16),    # prefill query length
