@@ -684,8 +684,17 @@ class LinearStep:
         dk_, dv_, dg, db = seq(c.n_doc, c.doc_len)
         self.doc_states = torch.empty((c.n_doc, h, d, d), dtype=torch.float32, device=dev)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # token-by-token form first (its time is reported beside the chunked one), then the chunked
+        # form whose states the step uses
         e0.record()
         msa.msa_gated_delta_rule(None, dk_, dv_, dg, db, final_state=self.doc_states, with_out=False)
+        e1.record()
+        torch.cuda.synchronize()
+        self.encode_recurrent_ms = e0.elapsed_time(e1)
+        msa.msa_gated_delta_rule_chunked(None, dk_, dv_, dg, db, final_state=self.doc_states, with_out=False)
+        torch.cuda.synchronize()
+        e0.record()
+        msa.msa_gated_delta_rule_chunked(None, dk_, dv_, dg, db, final_state=self.doc_states, with_out=False)
         e1.record()
         torch.cuda.synchronize()
         self.encode_ms = e0.elapsed_time(e1)
@@ -1214,7 +1223,9 @@ def main_linear(args):
         "config": {"workload": "linear-1M-decode-bf16", "n_docs": c.n_doc, "doc_len": c.doc_len, "batch": c.batch,
                    "q_len": c.q_len, "heads": c.heads_kv, "dk": c.dim, "dv": c.dim, "topk": c.topk,
                    "step": "route -> top-k -> state sum -> gated-delta step",
-                   "offline_document_states_ms": step.encode_ms},
+                   "offline_document_states_ms": step.encode_ms,
+                   "offline_document_states_form": "chunked (msa_gated_delta_rule_chunked)",
+                   "offline_document_states_ms_token_by_token": step.encode_recurrent_ms},
         "roofline": roof, "stages": stages,
         "cpu_baseline": None if args.no_cpu_baseline else step.cpu_baseline(),
     }

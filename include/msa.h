@@ -76,7 +76,8 @@ typedef enum msa_op {
   MSA_OP_TOPK_DOCS_EXCLUDING = 7,
   MSA_OP_ENCODE_DOCS = 8,
   MSA_OP_GDN_STATE_SUM = 9,
-  MSA_OP_GATED_DELTA_RULE = 10
+  MSA_OP_GATED_DELTA_RULE = 10,
+  MSA_OP_GATED_DELTA_RULE_CHUNKED = 11
 } msa_op;
 
 /* Version of this ABI (bumped on any incompatible change). */
@@ -393,6 +394,30 @@ msa_status msa_gated_delta_rule(const void* q, const void* k, const void* v, con
                                 float scale, const float* initial_state, int32_t batch, int32_t seq_len,
                                 int32_t heads, int32_t dk, int32_t dv, msa_dtype dt, void* out,
                                 float* final_state, void* stream);
+
+/* ------------------------------------------------------------------------
+ * The same rule in its chunked form (model card "Architecture summary": the
+ *     linear layers run the chunked gated delta rule, from the injected
+ *     state on the query side; the offline document encoding uses it too).
+ *
+ * Same arguments and result as msa_gated_delta_rule, computed 32 tokens at a
+ * time: inside a chunk the delta-rule writes solve a unit lower-triangular
+ * system (I + A) D = R, with A[t][j] = beta_t exp(G_t - G_j) (k_t . k_j)
+ * for j < t (G the running sum of g inside the chunk) and
+ * R = beta o (V - exp(G) o K S0); then S_C = exp(G_C) S0 + K^T (exp(G_C - G) o D)
+ * and O = scale (exp(G) o Q S0 + (M o Q K^T) D), M[t][j] = exp(G_t - G_j)
+ * for j <= t.  The contractions run on bf16 MFMA with float32 operands
+ * split into two bf16 terms, so the result agrees with the token-by-token
+ * form to about 1e-5 of the state's scale, not bit for bit.
+ *
+ * Supported: dt = MSA_BF16, dk = dv = 128 (other shapes return
+ * MSA_ERR_INVALID; msa_gated_delta_rule covers them).  q and k 16-byte
+ * aligned.  One workgroup per (sequence, head); no workspace.
+ * ---------------------------------------------------------------------- */
+msa_status msa_gated_delta_rule_chunked(const void* q, const void* k, const void* v, const float* g,
+                                        const float* beta, float scale, const float* initial_state,
+                                        int32_t batch, int32_t seq_len, int32_t heads, int32_t dk, int32_t dv,
+                                        msa_dtype dt, void* out, float* final_state, void* stream);
 
 #ifdef __cplusplus
 }

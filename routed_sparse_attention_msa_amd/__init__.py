@@ -14,7 +14,8 @@ of ``include/msa.h``; this package is its thin Python binding:
     msa_sparse_attn          S5/S6 sparse GQA attention (prefill and decode)
     msa_sparse_attn_backward its gradients (training through the routed layer)
     msa_gdn_state_sum        linear-layer variant: sum of the selected documents' states
-    msa_gated_delta_rule       and the gated delta rule from that initial state
+    msa_gated_delta_rule       and the gated delta rule from that initial state (token by token)
+    msa_gated_delta_rule_chunked  the same rule in its chunked form (MFMA, 32 tokens per chunk)
     msa_workspace_size       scratch bytes of any of these calls, by operation code
 """
 
@@ -25,6 +26,7 @@ from ._lib import (  # noqa: F401
     msa_chunk_offsets,
     msa_encode_docs,
     msa_gated_delta_rule,
+    msa_gated_delta_rule_chunked,
     msa_gather_kv,
     msa_gdn_state_sum,
     msa_pool_chunks,

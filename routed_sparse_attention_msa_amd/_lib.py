@@ -22,7 +22,7 @@ MSA_GATHER_CHECKED = 1
 MSA_GATHER_HOST_MEMCPY = 2
 (MSA_OP_POOL_CHUNKS, MSA_OP_ROUTE_SCORES, MSA_OP_TOPK_DOCS, MSA_OP_GATHER_KV, MSA_OP_SPARSE_ATTN,
  MSA_OP_SPARSE_ATTN_BACKWARD, MSA_OP_ROUTE_ROUNDS, MSA_OP_TOPK_DOCS_EXCLUDING, MSA_OP_ENCODE_DOCS,
- MSA_OP_GDN_STATE_SUM, MSA_OP_GATED_DELTA_RULE) = range(11)
+ MSA_OP_GDN_STATE_SUM, MSA_OP_GATED_DELTA_RULE, MSA_OP_GATED_DELTA_RULE_CHUNKED) = range(12)
 
 # Every entry point declared in include/msa.h: name -> (restype, argtypes).
 _STATUS = c_int
@@ -69,6 +69,9 @@ SIGNATURES = {
                                     c_void_p, c_void_p]),
     "msa_gated_delta_rule": (_STATUS, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_int32,
                                        c_int32, c_int32, c_int32, c_int32, c_int, c_void_p, c_void_p, c_void_p]),
+    "msa_gated_delta_rule_chunked": (_STATUS, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_void_p,
+                                               c_int32, c_int32, c_int32, c_int32, c_int32, c_int, c_void_p,
+                                               c_void_p, c_void_p]),
 }
 
 
@@ -550,10 +553,23 @@ def msa_gdn_state_sum(doc_states, topk_ids, s_ext=None):
 
 def msa_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None, out=None, final_state=None,
                          with_out=True, with_final_state=True):
-    """Gated delta rule over each sequence: q, k [batch, T, heads, dk]; v [batch, T, heads, dv];
+    """Gated delta rule over each sequence, token by token: q, k [batch, T, heads, dk]; v [batch, T, heads, dv];
     g (log decay), beta [batch, T, heads] float32; initial_state [batch, heads, dk, dv] float32 or None.
     Returns (out [batch, T, heads, dv] or None, final_state [batch, heads, dk, dv] float32 or None).
     ``q`` may be None when ``with_out`` is False (document encoding: final states only)."""
+    return _gated_delta_rule("msa_gated_delta_rule", q, k, v, g, beta, scale, initial_state, out, final_state,
+                             with_out, with_final_state)
+
+
+def msa_gated_delta_rule_chunked(q, k, v, g, beta, scale=None, initial_state=None, out=None, final_state=None,
+                                 with_out=True, with_final_state=True):
+    """The same rule in its chunked form (32 tokens per chunk on MFMA); bf16, dk = dv = 128 only.
+    Arguments and results as ``msa_gated_delta_rule``."""
+    return _gated_delta_rule("msa_gated_delta_rule_chunked", q, k, v, g, beta, scale, initial_state, out,
+                             final_state, with_out, with_final_state)
+
+
+def _gated_delta_rule(name, q, k, v, g, beta, scale, initial_state, out, final_state, with_out, with_final_state):
     _dev(k, "k", ndim=4)
     _dev(v, "v", dtype=k.dtype, ndim=4)
     _dev(g, "g", dtype=torch.float32, ndim=3)
@@ -584,7 +600,7 @@ def msa_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None, out=N
         _dev(final_state, "final_state", dtype=torch.float32)
         if final_state.shape != (batch, heads, dk, dv):
             raise ValueError("final_state must be [batch, heads, dk, dv]")
-    _check(lib().msa_gated_delta_rule(_ptr(q) if with_out else None, _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                      float(scale), _ptr(initial_state), batch, seq_len, heads, dk, dv,
-                                      _dtype_code(k), _ptr(out), _ptr(final_state), _stream(k.device)))
+    _check(getattr(lib(), name)(_ptr(q) if with_out else None, _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                float(scale), _ptr(initial_state), batch, seq_len, heads, dk, dv,
+                                _dtype_code(k), _ptr(out), _ptr(final_state), _stream(k.device)))
     return out, final_state

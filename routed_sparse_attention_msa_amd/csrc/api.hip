@@ -616,6 +616,7 @@ msa_status msa_workspace_size(int32_t op, const int64_t* dims, int32_t ndims, si
     case MSA_OP_GATHER_KV:
     case MSA_OP_GDN_STATE_SUM:
     case MSA_OP_GATED_DELTA_RULE:
+    case MSA_OP_GATED_DELTA_RULE_CHUNKED:
       *bytes = 0;  // these operations use no scratch
       return MSA_OK;
     case MSA_OP_ROUTE_SCORES:
@@ -673,6 +674,28 @@ msa_status msa_gated_delta_rule(const void* q, const void* k, const void* v, con
   return hip_status(msa::launch_gdn(q, k, v, g, beta, scale, initial_state, batch, seq_len, heads, dk, dv, dt, out,
                                     final_state, static_cast<hipStream_t>(stream)),
                     "msa_gated_delta_rule launch");
+}
+
+msa_status msa_gated_delta_rule_chunked(const void* q, const void* k, const void* v, const float* g,
+                                        const float* beta, float scale, const float* initial_state, int32_t batch,
+                                        int32_t seq_len, int32_t heads, int32_t dk, int32_t dv, msa_dtype dt,
+                                        void* out, float* final_state, void* stream) {
+  CHECK_ARG(dt == MSA_BF16, "the chunked form takes bf16 q / k / v (got dtype %d)", (int)dt);
+  CHECK_ARG(dk == 128 && dv == 128, "the chunked form takes dk = dv = 128 (got %d, %d)", dk, dv);
+  CHECK_ARG(batch > 0 && seq_len >= 0 && heads > 0, "sizes must be positive");
+  CHECK_ARG(batch <= 65535, "batch above 65535 is not supported");
+  CHECK_ARG(out != nullptr || final_state != nullptr, "nothing to compute: out and final_state are both NULL");
+  CHECK_ARG(scale == scale, "scale is NaN");
+  CHECK_ARG(seq_len == 0 || (k && v && g && beta && (out == nullptr || q)), "null tensor pointer");
+  CHECK_ARG(aligned16(k) && (out == nullptr || aligned16(q)), "q and k must be 16-byte aligned");
+  CHECK_ARG(((uintptr_t)v & 1u) == 0 && ((uintptr_t)out & 1u) == 0 && ((uintptr_t)g & 3u) == 0 &&
+                ((uintptr_t)beta & 3u) == 0 && ((uintptr_t)initial_state & 3u) == 0 &&
+                ((uintptr_t)final_state & 3u) == 0,
+            "tensors must be aligned to their element size");
+  if (seq_len == 0 && final_state == nullptr) return MSA_OK;
+  return hip_status(msa::launch_gdn_chunked(q, k, v, g, beta, scale, initial_state, batch, seq_len, heads, out,
+                                            final_state, static_cast<hipStream_t>(stream)),
+                    "msa_gated_delta_rule_chunked launch");
 }
 
 }  // extern "C"

@@ -150,5 +150,8 @@ hipError_t launch_gdn_state_sum(const float* states, const int32_t* ids, int bat
 hipError_t launch_gdn(const void* q, const void* k, const void* v, const float* g, const float* beta, float scale,
                       const float* init, int batch, int seq_len, int heads, int dk, int dv, msa_dtype dt,
                       void* out, float* final_state, hipStream_t s);
+hipError_t launch_gdn_chunked(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                              float scale, const float* init, int batch, int seq_len, int heads, void* out,
+                              float* final_state, hipStream_t s);
 
 }  // namespace msa

@@ -230,3 +230,19 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros((2, 64, 1, 8), dtype=torch.float32)
     with pytest.raises(ValueError, match="GPU tensor"):
         msa.msa_pool_chunks(x, 64)
+
+
+def test_gated_delta_rule_chunked_validation():
+    """The chunked form takes bf16 with dk = dv = 128 and rejects the rest on the host."""
+    lib = L.lib()
+    p = ctypes.c_void_p(4096)
+    args = lambda dt, dk, dv, q=p: (q, p, p, p, p, 0.1, None, 2, 64, 8, dk, dv, dt, p, p, None)
+    assert lib.msa_gated_delta_rule_chunked(*args(L.MSA_F32, 128, 128)) == L.MSA_ERR_INVALID
+    assert lib.msa_gated_delta_rule_chunked(*args(L.MSA_BF16, 64, 128)) == L.MSA_ERR_INVALID
+    assert lib.msa_gated_delta_rule_chunked(*args(L.MSA_BF16, 128, 64)) == L.MSA_ERR_INVALID
+    assert lib.msa_gated_delta_rule_chunked(*args(L.MSA_BF16, 128, 128, q=None)) == L.MSA_ERR_INVALID
+    assert lib.msa_gated_delta_rule_chunked(*args(L.MSA_BF16, 128, 128, q=ctypes.c_void_p(4098))) == L.MSA_ERR_INVALID
+    n = ctypes.c_size_t(7)
+    dims = (ctypes.c_int64 * 1)(0)
+    assert lib.msa_workspace_size(L.MSA_OP_GATED_DELTA_RULE_CHUNKED, dims, 0, ctypes.byref(n)) == L.MSA_OK
+    assert n.value == 0

@@ -90,6 +90,67 @@ def test_split_sequence_carries_the_state():
     np.testing.assert_allclose(to_f64(f2), to_f64(fs), rtol=0, atol=1e-5 * float(fs.abs().max()))
 
 
+@pytest.mark.parametrize("batch,t_len,heads,g_lo,with_init", [
+    (2, 100, 3, -0.5, True),     # three chunks and a ragged fourth
+    (1, 300, 2, -0.1, True),     # ten chunks: crosses a group of eight
+    (3, 1, 2, -0.5, True),       # one token
+    (1, 64, 1, -0.5, False),     # whole chunks, no initial state
+    (2, 37, 2, -0.5, False),
+    (1, 70, 2, -60.0, True),     # strong decay inside a chunk
+    (1, 40, 1, -300.0, True),    # decays that underflow float32 (state to zero)
+    (1, 513, 1, -0.05, True),    # two full groups and one token of a third
+])
+def test_gated_delta_rule_chunked_parity(batch, t_len, heads, g_lo, with_init):
+    """The chunked form against the oracle's token-by-token rule, outputs and final states."""
+    case(f"chunked gated delta rule B={batch} T={t_len} H={heads} g>={g_lo} init={with_init}")
+    q, k, v, g, beta, h0 = _seq(batch, t_len, heads, 128, 128, torch.bfloat16, seed=t_len + 7 * heads, g_lo=g_lo,
+                                with_init=with_init)
+    out, fs = msa.msa_gated_delta_rule_chunked(q, k, v, g, beta, initial_state=h0)
+    torch.cuda.synchronize()
+    ro, rh = gated_delta_rule(to_f64(q), to_f64(k), to_f64(v), to_f64(g), to_f64(beta),
+                              initial_state=None if h0 is None else to_f64(h0))
+    _check(out, fs, ro, rh, torch.bfloat16)
+
+
+def test_gated_delta_rule_chunked_empty_and_states_only():
+    """T = 0 returns the initial state; final states without outputs equal those with outputs."""
+    case("chunked gated delta rule: empty sequence, states only")
+    q, k, v, g, beta, h0 = _seq(2, 0, 2, 128, 128, torch.bfloat16, seed=5)
+    _, fs = msa.msa_gated_delta_rule_chunked(None, k, v, g, beta, initial_state=h0, with_out=False)
+    torch.cuda.synchronize()
+    assert torch.equal(fs, h0)
+    q, k, v, g, beta, h0 = _seq(3, 200, 2, 128, 128, torch.bfloat16, seed=6)
+    _, fs = msa.msa_gated_delta_rule_chunked(None, k, v, g, beta, initial_state=h0, with_out=False)
+    _, fs_full = msa.msa_gated_delta_rule_chunked(q, k, v, g, beta, initial_state=h0)
+    torch.cuda.synchronize()
+    assert (fs - fs_full).abs().max().item() <= 1e-6 * fs_full.abs().max().item()
+
+
+def test_document_states_chunked_full_bank():
+    """The offline encoding of the 1M-token bank's 2048 document states (512 tokens, 8 heads) in the
+    chunked form: sampled documents against the oracle, and every state against the token-by-token
+    kernel."""
+    case("chunked gated delta rule: 2048 documents x 512 tokens x 8 heads, states only")
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(11)
+    n_doc, t_len, heads, d = 2048, 512, 8, 128
+    k = torch.randn((n_doc, t_len, heads, d), generator=gen, device=DEV)
+    k = (k / torch.linalg.vector_norm(k, dim=-1, keepdim=True)).to(torch.bfloat16)
+    v = torch.randn((n_doc, t_len, heads, d), generator=gen, device=DEV).to(torch.bfloat16)
+    g = (torch.rand((n_doc, t_len, heads), generator=gen, device=DEV) * -0.5).contiguous()
+    beta = torch.rand((n_doc, t_len, heads), generator=gen, device=DEV).contiguous()
+    _, fs = msa.msa_gated_delta_rule_chunked(None, k, v, g, beta, with_out=False)
+    _, fr = msa.msa_gated_delta_rule(None, k, v, g, beta, with_out=False)
+    torch.cuda.synchronize()
+    rel = ((fs - fr).abs().amax(dim=(1, 2, 3)) / fr.abs().amax(dim=(1, 2, 3))).max().item()
+    print(f"  chunked vs token-by-token over all 2048 x 8 states: max err / max |h| {rel:.2e}")
+    assert rel <= 2e-4
+    for doc in (0, 777, n_doc - 1):
+        sl = slice(doc, doc + 1)
+        _, rh = gated_delta_rule(to_f64(k[sl]), to_f64(k[sl]), to_f64(v[sl]), to_f64(g[sl]), to_f64(beta[sl]))
+        _check(None, fs[sl], None, rh, torch.bfloat16)
+
+
 @pytest.mark.parametrize("n_docs,batch,k,heads,dk,dv", [
     (50, 3, 5, 2, 64, 64),
     (2048, 32, 16, 8, 128, 128),     # the 1M-token bank's states, a decode batch
