@@ -4,8 +4,8 @@
 // the selected documents' pooled K/V are loaded and placed next to the local
 // context; the content tier may live in host DRAM and be fetched on demand.
 //
-// One workgroup copies one selected document (its C pooled rows of K and V,
-// contiguous in the bank) with 16-byte loads and stores.  The source may be
+// One workgroup copies a 4 KiB slice of one selected document's C pooled rows
+// of K and V (contiguous in the bank) with 16-byte loads and stores.  The source may be
 // device memory or pinned host memory mapped into the GPU's address space
 // (then the loads travel over the host link with no host round trip).  Ids
 // outside [0, n_docs) are never dereferenced: their rows are zero-filled and
@@ -20,16 +20,19 @@ constexpr int kThreads = 256;
 
 __global__ __launch_bounds__(kThreads) void gather_kernel(
     const char* __restrict__ kbar, const char* __restrict__ vbar, const int32_t* __restrict__ ids,
-    int k, int64_t n_docs, size_t doc_bytes, char* __restrict__ k_sel, char* __restrict__ v_sel,
+    int k, int64_t n_docs, size_t doc_bytes, int slices, char* __restrict__ k_sel, char* __restrict__ v_sel,
     int* __restrict__ err_flag) {
-  const int b = blockIdx.y, i = blockIdx.x;
+  // one workgroup per (selected document, 4 KiB slice of its rows): every load
+  // of the copy is in flight at once (a loop over the slices waited for each)
+  const int b = blockIdx.y, i = blockIdx.x / slices, sl = blockIdx.x % slices;
   const int64_t id = ids[(size_t)b * k + i];
   const size_t dst = ((size_t)b * k + i) * doc_bytes;
   const bool ok = id >= 0 && id < n_docs;
   if (!ok && err_flag != nullptr && threadIdx.x == 0) atomicOr(err_flag, 1);
   const size_t src = ok ? (size_t)id * doc_bytes : 0;
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  for (size_t off = (size_t)threadIdx.x * 16; off < doc_bytes; off += (size_t)kThreads * 16) {
+  const size_t off = ((size_t)sl * kThreads + threadIdx.x) * 16;
+  if (off < doc_bytes) {
     const u32x4 kv = ok ? load16(kbar + src + off) : zero;
     const u32x4 vv = ok ? load16(vbar + src + off) : zero;
     store16(k_sel + dst + off, kv);
@@ -43,9 +46,11 @@ hipError_t launch_gather(const void* kbar, const void* vbar, const int32_t* ids,
                          int64_t n_docs, int cpd, size_t row_bytes, void* k_sel, void* v_sel,
                          int* err_flag, hipStream_t s) {
   const size_t doc_bytes = (size_t)cpd * row_bytes;
-  hipLaunchKernelGGL(gather_kernel, dim3(k, batch), dim3(kThreads), 0, s,
+  const size_t slices = (doc_bytes + kThreads * 16 - 1) / (kThreads * 16);
+  if ((size_t)k * slices > 0x7FFFFFFFu) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)(k * slices), batch), dim3(kThreads), 0, s,
                      static_cast<const char*>(kbar), static_cast<const char*>(vbar), ids, k, n_docs,
-                     doc_bytes, static_cast<char*>(k_sel), static_cast<char*>(v_sel), err_flag);
+                     doc_bytes, (int)slices, static_cast<char*>(k_sel), static_cast<char*>(v_sel), err_flag);
   return hipGetLastError();
 }
 

@@ -226,11 +226,36 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 
 // Largest 64-bit key of the wave (the high words first, then the low words
-// of the lanes that hold the largest high word).
+// of the lanes that hold the largest high word; when one lane holds it, its
+// low word is read directly).
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   const uint32_t hi = wave_max_u32((uint32_t)(v >> 32));
-  const uint32_t lo = wave_max_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u);
+  const uint64_t holders = __ballot((uint32_t)(v >> 32) == hi);
+  uint32_t lo;
+  if (__popcll(holders) == 1)   // uniform
+    lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, __ffsll((long long)holders) - 1);
+  else
+    lo = wave_max_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u);
   return ((uint64_t)hi << 32) | lo;
+}
+
+// Descending bitonic sort of one key per lane across the wave: lane r ends
+// with the r-th largest.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v, int lane) {
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1)
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint32_t xlo = (uint32_t)__shfl_xor((int)(uint32_t)v, stride);
+      const uint32_t xhi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), stride);
+      const uint64_t x = ((uint64_t)xhi << 32) | xlo;
+      // blocks of `size` lanes alternate direction; the last block (all 64) runs descending
+      const bool up = (lane & size) != 0 && size < 64;
+      const bool lower = (lane & stride) == 0;
+      const bool keep_max = lower != up;
+      v = keep_max ? (x > v ? x : v) : (x < v ? x : v);
+    }
+  return v;
 }
 
 // Descending bitonic sort of a register array (constant indices throughout).
@@ -299,11 +324,18 @@ __global__ __launch_bounds__(kThreads) void topk_small_kernel(
   if (lane < k) cand[wave][lane] = mine;
   __syncthreads();
   if (wave != 0) return;
-  uint64_t c[kThreads / 64];
+  uint64_t best;
+  if (k * (kThreads / 64) <= 64) {
+    // at most 64 candidates: one per lane (wave w's r-th at lane 16 w + r), then one cross-lane sort
+    const int w = lane >> 4, r = lane & 15;
+    best = wave_sort_desc(r < k ? cand[w][r] : 0, lane);
+  } else {
+    uint64_t c[kThreads / 64];
 #pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) c[w] = lane < k ? cand[w][lane] : 0;
-  sort_desc(c);
-  const uint64_t best = wave_extract(c, k, lane);
+    for (int w = 0; w < kThreads / 64; ++w) c[w] = lane < k ? cand[w][lane] : 0;
+    sort_desc(c);
+    best = wave_extract(c, k, lane);
+  }
   if (lane < k) {
     ids_out[(size_t)b * out_stride + lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)best);
     if (vals_out) vals_out[(size_t)b * out_stride + lane] = unorder_score((uint32_t)(best >> 32));

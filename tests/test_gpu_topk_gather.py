@@ -48,6 +48,27 @@ def test_topk_ties_and_signed_zero():
     assert ids[1, :4].tolist() == [0, 3, 4, 7]
 
 
+@pytest.mark.parametrize("n", [2048, 4096])
+@pytest.mark.parametrize("k", [1, 5, 16, 40, 64])
+def test_topk_small_path_ties(n, k):
+    """Rows of one tile (the routing and decode sizes): all-equal rows, signed zeros, -inf and
+    repeated values, against the oracle (ties to the lower id)."""
+    case(f"topk small path ties N={n} k={k}")
+    s = torch.full((4, n), 0.5, device=DEV)                                  # row 0: all equal
+    s[1] = torch.tensor([0.0, -0.0] * (n // 2), device=DEV)
+    s[1, 3::97] = 1.0                                                        # row 1: +-0 and a few ones
+    s[2] = float("-inf")
+    s[2, n - 1] = 2.0
+    s[2, 7] = 2.0                                                            # row 2: two equal maxima, rest -inf
+    g = torch.Generator(device=DEV)
+    g.manual_seed(n + k)
+    s[3] = torch.randint(0, 8, (n,), generator=g, device=DEV).float()        # row 3: eight values, many ties
+    ids, vals = _gpu_topk(s, k)
+    ref_ids, ref_vals = topk_docs(to_f64(s), k)
+    assert np.array_equal(ids, ref_ids)
+    assert np.array_equal(vals.astype(np.float64), ref_vals)
+
+
 def test_topk_infinities_and_all_equal():
     case("topk inf")
     s = torch.full((1, 9000), 0.25, device=DEV)
