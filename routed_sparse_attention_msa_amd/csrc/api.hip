@@ -484,8 +484,8 @@ msa_status msa_gather_kv(const void* kbar, const void* vbar, int32_t src_on_host
     if ((st = host_device_ptr(vbar, &src_v)) != MSA_OK) return st;
   }
   if (!(flags & MSA_GATHER_CHECKED)) {
-    e = msa::launch_gather(src_k, src_v, topk_ids, batch, k, n_docs, chunks_per_doc, row_bytes, k_sel,
-                           v_sel, nullptr, s);
+    e = msa::launch_gather(src_k, src_v, topk_ids, batch, k, n_docs, chunks_per_doc, row_bytes, src_on_host,
+                           k_sel, v_sel, nullptr, s);
     return hip_status(e, "msa_gather_kv launch");
   }
   // Checked: this call's own error word, cleared, raised by the kernel, read back.
@@ -494,8 +494,8 @@ msa_status msa_gather_kv(const void* kbar, const void* vbar, int32_t src_on_host
   if (st != MSA_OK) return st;
   Slot* sl = guard.slot();
   if ((e = hipMemsetAsync(sl->dev_flag, 0, sizeof(int), s)) != hipSuccess) return hip_status(e, "flag clear");
-  e = msa::launch_gather(src_k, src_v, topk_ids, batch, k, n_docs, chunks_per_doc, row_bytes, k_sel, v_sel,
-                         sl->dev_flag, s);
+  e = msa::launch_gather(src_k, src_v, topk_ids, batch, k, n_docs, chunks_per_doc, row_bytes, src_on_host, k_sel,
+                         v_sel, sl->dev_flag, s);
   if (e != hipSuccess) return hip_status(e, "msa_gather_kv launch");
   if ((e = hipMemcpyAsync(sl->host_flag, sl->dev_flag, sizeof(int), hipMemcpyDeviceToHost, s)) != hipSuccess)
     return hip_status(e, "flag read");

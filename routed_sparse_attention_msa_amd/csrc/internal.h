@@ -127,7 +127,7 @@ hipError_t launch_topk_excl(const float* scores, int batch, int64_t n_docs, int 
                             int64_t out_stride, void* ws, hipStream_t s);
 
 hipError_t launch_gather(const void* kbar, const void* vbar, const int32_t* ids, int batch, int k,
-                         int64_t n_docs, int cpd, size_t row_bytes, void* k_sel, void* v_sel,
+                         int64_t n_docs, int cpd, size_t row_bytes, bool host_src, void* k_sel, void* v_sel,
                          int* err_flag, hipStream_t s);
 
 size_t attn_workspace_bytes(int batch, int q_len, int heads_q, int heads_kv, int dim, int mem_len,
