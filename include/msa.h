@@ -410,7 +410,8 @@ msa_status msa_gated_delta_rule(const void* q, const void* k, const void* v, con
  * split into two bf16 terms, so the result agrees with the token-by-token
  * form to about 1e-5 of the state's scale, not bit for bit.
  *
- * Supported: dt = MSA_BF16, dk = dv = 128 (other shapes return
+ * Supported: dt = MSA_BF16, dk = dv = 128, and one sequence's rows
+ * (seq_len * heads * 256 bytes) spanning less than 4 GiB (other shapes return
  * MSA_ERR_INVALID; msa_gated_delta_rule covers them).  q and k 16-byte
  * aligned.  One workgroup per (sequence, head); no workspace.
  * ---------------------------------------------------------------------- */

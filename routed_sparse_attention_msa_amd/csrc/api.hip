@@ -684,6 +684,8 @@ msa_status msa_gated_delta_rule_chunked(const void* q, const void* k, const void
   CHECK_ARG(dk == 128 && dv == 128, "the chunked form takes dk = dv = 128 (got %d, %d)", dk, dv);
   CHECK_ARG(batch > 0 && seq_len >= 0 && heads > 0, "sizes must be positive");
   CHECK_ARG(batch <= 65535, "batch above 65535 is not supported");
+  CHECK_ARG((int64_t)seq_len * heads * 128 * 2 < ((int64_t)1 << 32),
+            "a sequence's rows (seq_len * heads * 256 bytes) must span less than 4 GiB");
   CHECK_ARG(out != nullptr || final_state != nullptr, "nothing to compute: out and final_state are both NULL");
   CHECK_ARG(scale == scale, "scale is NaN");
   CHECK_ARG(seq_len == 0 || (k && v && g && beta && (out == nullptr || q)), "null tensor pointer");

@@ -242,6 +242,10 @@ def test_gated_delta_rule_chunked_validation():
     assert lib.msa_gated_delta_rule_chunked(*args(L.MSA_BF16, 128, 64)) == L.MSA_ERR_INVALID
     assert lib.msa_gated_delta_rule_chunked(*args(L.MSA_BF16, 128, 128, q=None)) == L.MSA_ERR_INVALID
     assert lib.msa_gated_delta_rule_chunked(*args(L.MSA_BF16, 128, 128, q=ctypes.c_void_p(4098))) == L.MSA_ERR_INVALID
+    # a sequence spanning 4 GiB of rows (2^21 tokens x 8 heads x 256 B) would wrap the 32-bit buffer offsets
+    big = (p, p, p, p, p, 0.1, None, 1, 1 << 21, 8, 128, 128, L.MSA_BF16, p, p, None)
+    assert lib.msa_gated_delta_rule_chunked(*big) == L.MSA_ERR_INVALID
+    assert "4 GiB" in lib.msa_last_error().decode()
     n = ctypes.c_size_t(7)
     dims = (ctypes.c_int64 * 1)(0)
     assert lib.msa_workspace_size(L.MSA_OP_GATED_DELTA_RULE_CHUNKED, dims, 0, ctypes.byref(n)) == L.MSA_OK
