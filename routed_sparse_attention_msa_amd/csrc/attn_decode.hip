@@ -51,8 +51,15 @@ __device__ __forceinline__ int acc_row(int i, int hf) { return 8 * (i >> 2) + 4 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
 __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const bf16x2v v = {(__bf16)lo, (__bf16)hi};   // one v_cvt_pk_bf16_f32, round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
+// (aux 2: the non-temporal policy, as for the streamed rows of the other path)
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 2));
 }
 
 struct Rows {
@@ -73,6 +80,12 @@ struct KVRegs {
 // 32 keys, 16-byte segment lane & 15.
 __device__ __forceinline__ int krow_of(int st, int lane) { return 8 * (st & 3) + 2 * (lane >> 4) + (st >> 2); }
 
+// BLOCKS: the memory length is a multiple of 32, so each wave's 32 keys of a
+// split are all memory rows or all local rows: the loads go through one
+// buffer resource (chosen per wave and split) with 32-bit offsets, the row
+// part of every offset a scalar.  Otherwise each row's address is formed on
+// its own (64-bit, per lane).
+template <bool BLOCKS>
 __global__ __launch_bounds__(kWaves * 64, 1) void attn_decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_sel,
     const uint16_t* __restrict__ v_sel, int mem_len, const uint16_t* __restrict__ k_loc,
@@ -107,8 +120,35 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_decode_kernel(
   // to count them and make it wait for all of them): keys past the end read
   // the last key's row, whose scores are masked to -inf, so its V rows get
   // weight 0.
+  // per (sequence, KV head): memory and local rows behind buffer resources
+  // sized to them (rows past the end read as zeros; such keys are masked)
+  const uint32_t rs = (uint32_t)heads_kv * kD * 2;
+  const size_t sel0 = ((size_t)b * mem_len * heads_kv + g) * kD, loc0 = ((size_t)b * loc_len * heads_kv + g) * kD;
+  const uint32_t sel_bytes = (uint32_t)mem_len * rs - (uint32_t)g * kD * 2;
+  const uint32_t loc_bytes = (uint32_t)loc_len * rs - (uint32_t)g * kD * 2;
+  const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc((void*)(k_sel + (mem_len ? sel0 : 0)), (short)0, (int)(mem_len ? sel_bytes : 0u), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc((void*)(v_sel + (mem_len ? sel0 : 0)), (short)0, (int)(mem_len ? sel_bytes : 0u), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rkl = __builtin_amdgcn_make_buffer_rsrc((void*)(k_loc + loc0), (short)0, (int)loc_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rvl = __builtin_amdgcn_make_buffer_rsrc((void*)(v_loc + loc0), (short)0, (int)loc_bytes, kRsrcWord3);
+  // the lane's part of every offset: rows 2 (lane / 16) + ..., 16-byte segment lane % 16
+  const uint32_t lane_off = (uint32_t)(2 * (lane >> 4)) * rs + (lane & 15) * 16;
+
   auto load = [&](KVRegs& r, int sp) {
     const int k0 = sp * kSplitKeys + wave * 32;
+    if (BLOCKS) {
+      const bool in_mem = k0 < mem_len;           // uniform: the wave's 32 keys lie on one side
+      const __amdgpu_buffer_rsrc_t rk = in_mem ? rks : rkl, rv = in_mem ? rvs : rvl;
+      const int r0 = in_mem ? k0 : k0 - mem_len;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {               // V rows 2 (lane / 16) + 8 i and the next one
+        r.va[i] = bload(rv, lane_off + (uint32_t)(r0 + 8 * i) * rs);
+        r.vb[i] = bload(rv, lane_off + (uint32_t)(r0 + 8 * i + 1) * rs);
+      }
+#pragma unroll
+      for (int st = 0; st < 8; ++st)              // K row krow_of(st, lane)
+        r.kw[st] = bload(rk, lane_off + (uint32_t)(r0 + 8 * (st & 3) + (st >> 2)) * rs);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int task = lane + 64 * i;
@@ -401,12 +441,21 @@ hipError_t launch_attn_decode(const void* q, const void* k_sel, const void* v_se
   const size_t smem_v = (size_t)kWaves * (kVRegionWords * 4 + kKRegionBytes);
   const size_t smem_c = ((size_t)kWaves * nq * kD + (size_t)kWaves * nq * 2) * 4;
   const size_t smem = smem_v > smem_c ? smem_v : smem_c;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(attn_decode_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)(kWaves * (32 * kD + 64) * 4 > (int)smem_v ? kWaves * (32 * kD + 64) * 4 : (int)smem_v));
+  static const hipError_t attr = [] {
+    const int bytes = kWaves * (32 * kD + 64) * 4 > (int)((size_t)kWaves * (kVRegionWords * 4 + kKRegionBytes))
+                          ? kWaves * (32 * kD + 64) * 4
+                          : (int)((size_t)kWaves * (kVRegionWords * 4 + kKRegionBytes));
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_decode_kernel<true>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_decode_kernel<false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    return e;
+  }();
   if (attr != hipSuccess) return attr;
   const unsigned grid = (unsigned)((size_t)batch * heads_kv * n_part);
-  hipLaunchKernelGGL(attn_decode_kernel, dim3(grid), dim3(kWaves * 64), smem, s,
+  auto kern = mem_len % 32 == 0 ? attn_decode_kernel<true> : attn_decode_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kWaves * 64), smem, s,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_sel),
                      static_cast<const uint16_t*>(v_sel), mem_len, static_cast<const uint16_t*>(k_loc),
                      static_cast<const uint16_t*>(v_loc), loc_len, batch, q_len, heads_q, heads_kv,

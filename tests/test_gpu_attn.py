@@ -62,6 +62,7 @@ def _check(q, ks, vs, kl, vl, rtol, lse_atol):
     (1, 40, 8, 2, 128, 0, 90, torch.bfloat16),         #   first queries' causal limit (all masked)
     (32, 1, 32, 8, 128, 32, 250, torch.bfloat16),      # decode, one workgroup per (sequence, KV head)
     (40, 2, 16, 8, 128, 16, 90, torch.bfloat16),       # more pairs than CUs, 2 tokens
+    (2, 1, 32, 8, 128, 40, 1000, torch.bfloat16),      # decode, memory length not a multiple of 32 (per-row loads)
     (1, 1, 8, 1, 128, 64, 5000, torch.bfloat16),       # one pair: many runs of splits, combined
     (1, 96, 8, 2, 128, 64, 160, torch.bfloat16),       # 3 token blocks: a block pair and a middle block alone
     (1, 80, 16, 2, 128, 40, 100, torch.bfloat16),      # group of 8 heads (two head sub-groups), partial tiles
