@@ -209,14 +209,17 @@ def kernel_source_sha(src_files):
 
 INTERLEAVE_ROUNDS = 3
 
-# stage -> (kernel-name patterns separated by |, source file[, launches of each kernel per stage call])
+# stage -> (kernel-name patterns separated by |, source file[, launches of each kernel per stage call:
+#           one count for all, or a count per pattern])
 STAGE_KERNELS = {
     "prefill": {"pool": ("pool_kernel", "pool.hip"), "route": ("route_", "route.hip"),
                 "topk": ("topk", "topk.hip"), "gather": ("gather", "gather.hip"),
                 "attn": ("attn_prefill", "attn_prefill.hip")},
     "decode": {"route": ("route_", "route.hip"), "topk": ("topk", "topk.hip"),
                "gather": ("gather", "gather.hip"), "attn": ("attn_decode", "attn_decode.hip")},
-    "interleave": {"rounds": ("route_|topk", "route.hip|topk.hip", INTERLEAVE_ROUNDS), "gather": ("gather", "gather.hip"),
+    # (the rounds' routing is one launch over all rounds' queries; each round has its own top-k launch)
+    "interleave": {"rounds": ("route_|topk", "route.hip|topk.hip", {"route_": 1, "topk": INTERLEAVE_ROUNDS}),
+                   "gather": ("gather", "gather.hip"),
                    "attn": ("attn_prefill", "attn_prefill.hip")},
     "backward": {"attn": ("attn_prefill", "attn_prefill.hip"), "attn_bwd": ("attn_bwd", "attn_backward.hip")},
     # (the backward stage is two kernels, dq then dk/dv; its entry covers both)
@@ -310,8 +313,14 @@ def summarize_traffic(d):
             names = sorted(k for k in fm if "msa::" in k and any(p in k for p in pat.split("|")))
             if not names:
                 continue
-            rd = per_call * sum(fm[k] for k in names) * 1024 * fetch_factor
-            wr = per_call * sum(wm.get(k, 0.0) for k in names) * 1024 * write_factor
+
+            def launches(name):
+                if isinstance(per_call, dict):
+                    return next(n for p, n in per_call.items() if p in name)
+                return per_call
+
+            rd = sum(launches(k) * fm[k] for k in names) * 1024 * fetch_factor
+            wr = sum(launches(k) * wm.get(k, 0.0) for k in names) * 1024 * write_factor
             out[wl][stage] = {"source_sha": kernel_source_sha(src), "read_bytes": rd, "write_bytes": wr,
                               "bytes_per_launch": rd + wr, "kernels": names}
             short = ", ".join(sorted({_short_kernel(n) for n in names}))

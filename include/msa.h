@@ -244,7 +244,10 @@ msa_status msa_topk_docs(const float* doc_scores, int32_t batch, int64_t n_docs,
  *
  * msa_route_rounds: `rounds` rounds on `stream`; round r routes
  *   q_r[r] as msa_route_scores does, then keeps the top-k of the documents no
- *   earlier round selected (msa_topk_docs_excluding).
+ *   earlier round selected (msa_topk_docs_excluding).  A round's scores do
+ *   not depend on the earlier picks, so when the tiled routing kernel takes
+ *   both shapes the routing of all rounds runs as one launch over
+ *   rounds*batch sequences (same results as round-by-round calls).
  *   q_r          [rounds, batch, q_len, heads, dim]  (dtype dt)
  *   kbar_r, kbar_r_norm as for msa_route_scores
  *   topk_ids     [batch, rounds*k] int32 output: round r in columns [r*k, (r+1)*k)

@@ -346,6 +346,18 @@ msa_status msa_topk_docs_excluding(const float* doc_scores, int32_t batch, int64
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Every round's router queries are given up front and a round's scores do not
+// depend on the earlier rounds' picks, so all rounds can be routed in one
+// launch over rounds*batch sequences -- done when the tiled kernel routes both
+// that launch and a single round (its scores of a sequence are then the same
+// bits as a round's own call; the other paths may order a sum differently for
+// another number of sequences).
+static bool rounds_fused(int32_t rounds, int32_t batch, int32_t q_len, int32_t heads, int32_t dim, int32_t cpd,
+                         msa_dtype dt) {
+  return rounds > 1 && (int64_t)rounds * batch <= 65535 && msa::route_is_tiled(batch, q_len, heads, dim, cpd, dt) &&
+         msa::route_is_tiled(rounds * batch, q_len, heads, dim, cpd, dt);
+}
+
 static msa_status rounds_workspace(int32_t rounds, int32_t batch, int32_t q_len, int32_t heads,
                                    int32_t dim, int64_t n_docs, int32_t cpd, int32_t k, msa_dtype dt,
                                    size_t* scores_bytes, size_t* total) {
@@ -355,9 +367,11 @@ static msa_status rounds_workspace(int32_t rounds, int32_t batch, int32_t q_len,
   CHECK_ARG(rounds >= 1 && (int64_t)rounds * k <= n_docs,
             "need rounds >= 1 and rounds*k <= n_docs (rounds=%d k=%d n_docs=%lld)", rounds, k,
             (long long)n_docs);
-  *scores_bytes = align256((size_t)batch * (size_t)n_docs * sizeof(float));
-  *total = *scores_bytes + std::max(msa::route_workspace_bytes(batch, q_len, heads, dim, n_docs, cpd, dt),
-                                    msa::topk_workspace_bytes(batch, n_docs, k));
+  *scores_bytes = align256((size_t)rounds * batch * (size_t)n_docs * sizeof(float));
+  const size_t route_ws = rounds_fused(rounds, batch, q_len, heads, dim, cpd, dt)
+                              ? msa::route_workspace_bytes(rounds * batch, q_len, heads, dim, n_docs, cpd, dt)
+                              : msa::route_workspace_bytes(batch, q_len, heads, dim, n_docs, cpd, dt);
+  *total = *scores_bytes + std::max(route_ws, msa::topk_workspace_bytes(batch, n_docs, k));
   return MSA_OK;
 }
 
@@ -388,16 +402,25 @@ msa_status msa_route_rounds(const void* q_r, const void* kbar_r, const float* kb
   CHECK_ARG(ws_bytes >= total, "workspace too small (%zu < %zu bytes)", ws_bytes, total);
   CHECK_ARG(ws != nullptr && aligned16(ws), "workspace pointer missing or misaligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* scores = static_cast<float*>(ws);
+  float* scores = static_cast<float*>(ws);      // [rounds][batch][n_docs]
   void* scratch = static_cast<char*>(ws) + sb;
-  const size_t q_bytes = (size_t)batch * q_len * heads * dim * dtype_size(dt);
   const int64_t stride = (int64_t)rounds * k;
-  for (int r = 0; r < rounds; ++r) {
-    const void* q = static_cast<const char*>(q_r) + (size_t)r * q_bytes;
-    hipError_t e = msa::launch_route(q, kbar_r, kbar_r_norm, batch, q_len, heads, dim, n_docs,
-                                     chunks_per_doc, dt, scores, scratch, s);
+  const size_t q_bytes = (size_t)batch * q_len * heads * dim * dtype_size(dt);
+  const bool fused = rounds_fused(rounds, batch, q_len, heads, dim, chunks_per_doc, dt);
+  hipError_t e = hipSuccess;
+  if (fused) {   // all rounds' scores in one routing launch: q_r is [rounds * batch] sequences
+    e = msa::launch_route(q_r, kbar_r, kbar_r_norm, rounds * batch, q_len, heads, dim, n_docs, chunks_per_doc,
+                          dt, scores, scratch, s);
     if (e != hipSuccess) return hip_status(e, "msa_route_rounds route launch");
-    e = msa::launch_topk_excl(scores, batch, n_docs, k, topk_ids, r * k, stride, topk_ids + (size_t)r * k,
+  }
+  for (int r = 0; r < rounds; ++r) {
+    float* sc = scores + (size_t)r * batch * n_docs;
+    if (!fused) {
+      e = msa::launch_route(static_cast<const char*>(q_r) + (size_t)r * q_bytes, kbar_r, kbar_r_norm, batch, q_len,
+                            heads, dim, n_docs, chunks_per_doc, dt, sc, scratch, s);
+      if (e != hipSuccess) return hip_status(e, "msa_route_rounds route launch");
+    }
+    e = msa::launch_topk_excl(sc, batch, n_docs, k, topk_ids, r * k, stride, topk_ids + (size_t)r * k,
                               topk_scores ? topk_scores + (size_t)r * k : nullptr, stride, scratch, s);
     if (e != hipSuccess) return hip_status(e, "msa_route_rounds top-k launch");
   }

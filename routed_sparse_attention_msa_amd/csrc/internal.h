@@ -106,6 +106,9 @@ hipError_t launch_encode(const void* x, void* xbar, float* norm, const int64_t* 
                          int64_t total_chunks, int chunk, int heads, int dim, float rope_base,
                          msa_dtype dt, hipStream_t s);
 
+// Whether routing this shape takes the tiled MFMA kernel (whose scores for a
+// sequence do not depend on the other sequences of the launch).
+bool route_is_tiled(int batch, int q_len, int heads, int dim, int cpd, msa_dtype dt);
 size_t route_workspace_bytes(int batch, int q_len, int heads, int dim, int64_t n_docs, int cpd,
                              msa_dtype dt);
 hipError_t launch_route(const void* q_r, const void* kbar_r, const float* knorm, int batch,

@@ -886,6 +886,10 @@ hipError_t launch_route_generic(const void* q_r, const void* kbar_r, const float
                                 int q_len, int heads, int dim, int64_t n_docs, int cpd,
                                 msa_dtype dt, float* doc_scores, hipStream_t s);
 
+bool route_is_tiled(int batch, int q_len, int heads, int dim, int cpd, msa_dtype dt) {
+  return pick(batch, q_len, heads, dim, cpd, dt) == RoutePath::Tiled;
+}
+
 size_t route_workspace_bytes(int batch, int q_len, int heads, int dim, int64_t n_docs, int cpd,
                              msa_dtype dt) {
   if (pick(batch, q_len, heads, dim, cpd, dt) != RoutePath::Tiled) return 0;

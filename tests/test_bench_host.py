@@ -84,3 +84,33 @@ def test_source_hash_follows_included_headers(tmp_path, monkeypatch):
     (src / "common.h").write_text("int c = 2;\n")
     h2 = b.kernel_source_sha("k.hip")
     assert h1 != h2
+
+
+def test_traffic_summary_counts_each_kernels_launches(tmp_path, monkeypatch):
+    """A stage's bytes per call sum its kernels' per-launch counters times their launches per call: the
+    interleave rounds run one routing launch (all rounds' queries) and one top-k launch per round."""
+    import csv
+    import json
+    b = _bench()
+    monkeypatch.setattr(b, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    d = tmp_path / "traffic"
+
+    def write(name, rows):
+        p = d / name / "run"
+        p.mkdir(parents=True)
+        with open(p / "run_counter_collection.csv", "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Value"])
+            w.writeheader()
+            for k, v in rows:
+                w.writerow({"Kernel_Name": k, "Counter_Value": v})
+
+    gib_kib = (1 << 30) / 1024
+    for kind in ("fetch", "write"):
+        write(f"copy_{kind}", [("void at::native::neg_kernel", gib_kib)])
+        write(f"interleave_{kind}", [("msa::(anonymous namespace)::route_tiled_kernel(int)", 1000.0),
+                                     ("msa::(anonymous namespace)::topk_small_kernel<8>(int)", 10.0)])
+    b.summarize_traffic(str(d))
+    rec = json.load(open(tmp_path / "profiles" / "traffic.json"))["interleave"]["rounds"]
+    assert abs(rec["read_bytes"] - (1000.0 + 3 * 10.0) * 1024) < 1e-6
+    assert abs(rec["bytes_per_launch"] - 2 * (1000.0 + 3 * 10.0) * 1024) < 1e-6

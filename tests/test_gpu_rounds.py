@@ -145,6 +145,25 @@ def test_route_rounds_fixed_query_is_one_larger_topk():
     assert torch.equal(ids, one_ids) and torch.equal(vals, one_vals)
 
 
+@pytest.mark.parametrize("batch,q_len", [(2, 256), (1, 512)])
+def test_route_rounds_fused_launch_matches_separate_calls(batch, q_len):
+    """Shapes the tiled kernel routes both per round and for all rounds together: the rounds' routing
+    runs as one launch, and its picks and scores equal round-by-round calls bit for bit (one 256-row
+    tile per sequence, and sequences over two tiles merged by atomic maxima)."""
+    case(f"route rounds, one routing launch: B={batch} T={q_len}")
+    cpd, k, rounds = 8, 16, 3
+    kbar, norm = _bank(1000, cpd, 8, 128, seed=10)
+    q = _planted_queries(kbar, cpd, rounds, batch, q_len, seed=11, docs_per_round=8)
+    ids, vals = msa.msa_route_rounds(q, kbar, norm, cpd, k)
+    prev = torch.full((batch, 1), -1, dtype=torch.int32, device=DEV)
+    for r in range(rounds):
+        s = msa.msa_route_scores(q[r], kbar, norm, cpd)
+        i_r, v_r = msa.msa_topk_docs_excluding(s, k, prev)
+        assert torch.equal(i_r, ids[:, r * k:(r + 1) * k]) and torch.equal(v_r, vals[:, r * k:(r + 1) * k])
+        prev = ids[:, :(r + 1) * k].contiguous()
+    torch.cuda.synchronize()
+
+
 def test_route_rounds_matches_separate_calls():
     """msa_route_rounds equals route + top-k-excluding called round by round."""
     case("route rounds vs separate calls")
