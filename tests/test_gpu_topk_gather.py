@@ -49,7 +49,7 @@ def test_topk_ties_and_signed_zero():
 
 
 @pytest.mark.parametrize("n", [2048, 4096])
-@pytest.mark.parametrize("k", [1, 5, 16, 40, 64])
+@pytest.mark.parametrize("k", [1, 5, 12, 16, 40, 64])
 def test_topk_small_path_ties(n, k):
     """Rows of one tile (the routing and decode sizes): all-equal rows, signed zeros, -inf and
     repeated values, against the oracle (ties to the lower id)."""
