@@ -338,6 +338,33 @@ msa_status msa_sparse_attn(const void* q, const void* k_sel, const void* v_sel, 
                            size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Merge of two partial attentions over disjoint key sets (the attention of
+ *     S5/S6 runs over [selected memory rows ; local rows], model card
+ *     "Architecture summary" and README "Inference Pipeline" stage 3; a
+ *     softmax over a union of disjoint key sets is the log-sum-exp weighted
+ *     sum of the softmaxes over each set).
+ *
+ * For every (b, t, h), with la = lse_a[b,h,t], lb = lse_b[b,h,t]:
+ *   lse[b,h,t] = log(exp(la) + exp(lb))
+ *   out[b,t,h] = exp(la - lse) out_a[b,t,h] + exp(lb - lse) out_b[b,t,h]
+ * A part with lse -inf (no visible key) has weight 0; with both at -inf,
+ * out is 0 and lse is -inf.  Use: a decode step's local rows do not depend
+ * on routing, so msa_sparse_attn over them (mem_len = 0) can run on a second
+ * stream beside route, top-k and gather; the selected memory rows' attention
+ * follows the gather, and this call combines the two.  (With q_len = 1 the
+ * memory rows may be passed as the local rows of a call with mem_len = 0:
+ * the one token sees every local row.)
+ *
+ * out_a, out_b, out  [batch, q_len, heads_q, dim]  dtype dt, 16-byte aligned
+ * lse_a, lse_b       [batch, heads_q, q_len]  float32 (natural log)
+ * lse                [batch, heads_q, q_len]  float32 output, or NULL
+ * out may alias out_a or out_b, lse may alias lse_a or lse_b.  No workspace.
+ * ---------------------------------------------------------------------- */
+msa_status msa_attn_merge(const void* out_a, const float* lse_a, const void* out_b, const float* lse_b,
+                          int32_t batch, int32_t q_len, int32_t heads_q, int32_t dim, msa_dtype dt, void* out,
+                          float* lse, void* stream);
+
+/* ------------------------------------------------------------------------
  * Backward of the sparse attention (MSA README "Abstract" and Figure 1
  *     caption: top-k selection fused with a sparse attention that stays
  *     end-to-end differentiable; model card "Training (CPT)": the router and

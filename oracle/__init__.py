@@ -38,6 +38,7 @@ from .msa_oracle import (
     gather_kv,
     sparse_attention,
     sparse_attention_rows,
+    merge_attention,
     sparse_attention_backward,
     gated_delta_rule,
     inject_states,
@@ -61,6 +62,7 @@ __all__ = [
     "gather_kv",
     "sparse_attention",
     "sparse_attention_rows",
+    "merge_attention",
     "sparse_attention_backward",
     "gated_delta_rule",
     "inject_states",

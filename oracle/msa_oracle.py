@@ -382,6 +382,35 @@ def sparse_attention(q, k_sel, v_sel, k_loc, v_loc, scale=None):
     return o, lse
 
 
+def merge_attention(o_a, lse_a, o_b, lse_b):
+    """Attention over the union of two disjoint key sets, from the attention over each.
+
+    The attention of [Card] "Architecture summary" / [Pipeline] stage 3 runs
+    over the memory rows followed by the local rows; split into two disjoint
+    key sets A and B, the softmax over A u B weights each part by its share of
+    the normaliser: with lse_X = log sum_{j in X} exp(l_j),
+
+        lse = log(exp(lse_a) + exp(lse_b)),
+        o   = exp(lse_a - lse) o_a + exp(lse_b - lse) o_b.
+
+    A part with lse = -inf holds no visible key and gets weight 0; when both
+    are -inf the result is o = 0, lse = -inf (a reading: nothing is visible).
+
+    o_* [B, T, H, d], lse_* [B, H, T]; returns (o float64, lse float64).
+    """
+    o_a = np.asarray(o_a, dtype=np.float64)
+    o_b = np.asarray(o_b, dtype=np.float64)
+    lse_a = np.asarray(lse_a, dtype=np.float64)
+    lse_b = np.asarray(lse_b, dtype=np.float64)
+    lse = np.logaddexp(lse_a, lse_b)
+    empty = np.isneginf(lse)
+    safe = np.where(empty, 0.0, lse)
+    w_a = np.where(empty, 0.0, np.exp(lse_a - safe))          # [B, H, T]
+    w_b = np.where(empty, 0.0, np.exp(lse_b - safe))
+    to_o = lambda w: np.transpose(w, (0, 2, 1))[..., None]     # -> [B, T, H, 1]
+    return to_o(w_a) * o_a + to_o(w_b) * o_b, lse
+
+
 # ---------------------------------------------------------------------------
 # Backward of the sparse attention (the method is trained end to end)
 # ---------------------------------------------------------------------------

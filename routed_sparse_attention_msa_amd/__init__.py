@@ -12,6 +12,7 @@ of ``include/msa.h``; this package is its thin Python binding:
     msa_route_rounds         multi-round routing (Memory Interleave)
     msa_gather_kv            S4  gather (or host-tier fetch) of the selected pooled K/V
     msa_sparse_attn          S5/S6 sparse GQA attention (prefill and decode)
+    msa_attn_merge           log-sum-exp merge of two partial attentions (disjoint key sets)
     msa_sparse_attn_backward its gradients (training through the routed layer)
     msa_gdn_state_sum        linear-layer variant: sum of the selected documents' states
     msa_gated_delta_rule       and the gated delta rule from that initial state (token by token)
@@ -23,6 +24,7 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     MsaError,
     lib,
+    msa_attn_merge,
     msa_chunk_offsets,
     msa_encode_docs,
     msa_gated_delta_rule,

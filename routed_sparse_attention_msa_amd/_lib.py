@@ -59,6 +59,8 @@ SIGNATURES = {
     "msa_sparse_attn": (_STATUS, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
                                   c_int32, c_int32, c_int32, c_int32, c_int32, c_float, c_int,
                                   c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "msa_attn_merge": (_STATUS, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
+                                 c_int, c_void_p, c_void_p, c_void_p]),
     "msa_sparse_attn_backward_workspace": (_STATUS, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                                                      c_int32, c_int, POINTER(c_size_t)]),
     "msa_sparse_attn_backward": (_STATUS, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
@@ -471,6 +473,32 @@ def msa_sparse_attn(q, k_sel, v_sel, k_loc, v_loc, scale=None, out=None, lse=Non
                                  loc_len, batch, q_len, heads_q, heads_kv, dim, float(scale),
                                  _dtype_code(q), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
                                  _stream(q.device)))
+    return out, lse
+
+
+def msa_attn_merge(out_a, lse_a, out_b, lse_b, out=None, lse=None, with_lse=True):
+    """Log-sum-exp merge of two partial attentions over disjoint key sets:
+    ``out_*`` [batch, q_len, heads_q, dim], ``lse_*`` [batch, heads_q, q_len] float32
+    -> (out, lse or None).  ``out`` may be ``out_a`` or ``out_b`` and ``lse`` may be
+    ``lse_a`` or ``lse_b`` (in place)."""
+    _dev(out_a, "out_a", ndim=4)
+    _dev(out_b, "out_b", dtype=out_a.dtype)
+    _shape(out_b, "out_b", out_a.shape)
+    batch, q_len, heads_q, dim = out_a.shape
+    for t, name in ((lse_a, "lse_a"), (lse_b, "lse_b")):
+        _dev(t, name, dtype=torch.float32)
+        _shape(t, name, (batch, heads_q, q_len))
+    if out is None:
+        out = torch.empty_like(out_a)
+    _dev(out, "out", dtype=out_a.dtype)
+    _shape(out, "out", out_a.shape)
+    if with_lse and lse is None:
+        lse = torch.empty_like(lse_a)
+    if lse is not None:
+        _dev(lse, "lse", dtype=torch.float32)
+        _shape(lse, "lse", (batch, heads_q, q_len))
+    _check(lib().msa_attn_merge(_ptr(out_a), _ptr(lse_a), _ptr(out_b), _ptr(lse_b), batch, q_len, heads_q, dim,
+                                _dtype_code(out_a), _ptr(out), _ptr(lse), _stream(out_a.device)))
     return out, lse
 
 

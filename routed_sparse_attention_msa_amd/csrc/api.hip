@@ -580,6 +580,22 @@ msa_status msa_sparse_attn(const void* q, const void* k_sel, const void* v_sel, 
                     "msa_sparse_attn launch");
 }
 
+msa_status msa_attn_merge(const void* out_a, const float* lse_a, const void* out_b, const float* lse_b,
+                          int32_t batch, int32_t q_len, int32_t heads_q, int32_t dim, msa_dtype dt, void* out,
+                          float* lse, void* stream) {
+  CHECK_ARG(valid_dtype(dt), "unknown dtype %d", (int)dt);
+  CHECK_ARG(batch > 0 && q_len > 0 && heads_q > 0 && dim > 0, "sizes must be positive");
+  CHECK_ARG(dim <= 256, "dim %d above 256 is not supported", dim);
+  CHECK_ARG(((size_t)dim * dtype_size(dt)) % 16 == 0, "dim*sizeof(dtype) must be a multiple of 16");
+  CHECK_ARG(out_a && lse_a && out_b && lse_b && out, "null tensor pointer");
+  CHECK_ARG(aligned16(out_a) && aligned16(out_b) && aligned16(out), "out_a, out_b and out must be 16-byte aligned");
+  CHECK_ARG(((uintptr_t)lse_a & 3u) == 0 && ((uintptr_t)lse_b & 3u) == 0 && ((uintptr_t)lse & 3u) == 0,
+            "lse arrays must be 4-byte aligned");
+  return hip_status(msa::launch_attn_merge(out_a, lse_a, out_b, lse_b, batch, q_len, heads_q, dim, dt, out, lse,
+                                           static_cast<hipStream_t>(stream)),
+                    "msa_attn_merge launch");
+}
+
 msa_status msa_sparse_attn_backward_workspace(int32_t batch, int32_t q_len, int32_t heads_q,
                                               int32_t heads_kv, int32_t dim, int32_t mem_len,
                                               int32_t loc_len, msa_dtype dt, size_t* bytes) {

@@ -140,6 +140,11 @@ hipError_t launch_attn(const void* q, const void* k_sel, const void* v_sel, int 
                        int heads_q, int heads_kv, int dim, float scale, msa_dtype dt, void* out,
                        float* lse, void* ws, hipStream_t s);
 
+// Log-sum-exp merge of two partial attentions over disjoint key sets.
+hipError_t launch_attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                             int batch, int q_len, int heads_q, int dim, msa_dtype dt, void* o, float* lse,
+                             hipStream_t s);
+
 size_t attn_backward_workspace_bytes(int batch, int q_len, int heads_q, int heads_kv, int dim, int mem_len,
                                      int loc_len, msa_dtype dt);
 hipError_t launch_attn_backward(const void* q, const void* k_sel, const void* v_sel, int mem_len,

@@ -149,6 +149,29 @@ def test_attn_validation():
                                0, None) == L.MSA_ERR_INVALID
 
 
+def test_attn_merge_validation():
+    lib = msa.lib()
+    p, f = ctypes.c_void_p(256), ctypes.c_void_p(260)
+    ok = (p, f, p, f, 2, 1, 32, 128, L.MSA_BF16, p, f, None)
+    def call(*args):
+        return lib.msa_attn_merge(*args)
+    bad = list(ok); bad[8] = 7                        # unknown dtype
+    assert call(*bad) == L.MSA_ERR_INVALID
+    bad = list(ok); bad[7] = 512                      # dim above 256
+    assert call(*bad) == L.MSA_ERR_INVALID
+    bad = list(ok); bad[7] = 100                      # 200 bytes per row: not whole 16-byte pieces
+    assert call(*bad) == L.MSA_ERR_INVALID
+    bad = list(ok); bad[4] = 0                        # empty batch
+    assert call(*bad) == L.MSA_ERR_INVALID
+    bad = list(ok); bad[2] = None                     # missing input
+    assert call(*bad) == L.MSA_ERR_INVALID
+    bad = list(ok); bad[9] = ctypes.c_void_p(264)     # output not 16-byte aligned
+    assert call(*bad) == L.MSA_ERR_INVALID
+    bad = list(ok); bad[1] = ctypes.c_void_p(258)     # lse not 4-byte aligned
+    assert call(*bad) == L.MSA_ERR_INVALID
+    assert "aligned" in _err()
+
+
 def test_attn_rejects_spans_of_4gib():
     """One sequence's memory or local rows must span less than 4 GiB (the
     kernels' buffer offsets are 32-bit)."""

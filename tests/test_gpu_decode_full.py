@@ -71,3 +71,35 @@ def test_decode_step_full_size(decode_inputs, topk):
     print(f"  attention: max row rel-L2 {rel.max():.2e} over {rel.size} rows, max |lse err| {lerr.max():.2e}")
     assert rel.shape == (32, 1, 32) and rel.max() <= ATTN_RTOL_BF16
     assert lerr.max() <= 2e-3
+
+
+def test_decode_step_full_size_overlapped(decode_inputs):
+    """The overlapped form the decode bench times: attention over the 4096
+    local rows on a second stream beside route -> top-k -> gather, then the
+    128 memory rows' attention (passed as the local rows of a call without
+    memory: the one token sees them all) and the log-sum-exp merge.  All 1,024
+    (sequence, head) rows against the oracle's attention over [memory ; local]."""
+    cfg = mi.DECODE
+    x = decode_inputs
+    cpd, topk = cfg.chunks_per_doc, cfg.topk
+    case("decode full, overlapped: local attention on a second stream, memory attention + merge after the gather")
+    cur, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    o_loc = torch.empty_like(x["q"])
+    l_loc = torch.empty((cfg.batch, cfg.heads_q, 1), dtype=torch.float32, device=DEV)
+    side.wait_stream(cur)
+    with torch.cuda.stream(side):
+        msa.msa_sparse_attn(x["q"], None, None, x["k_loc"], x["v_loc"], out=o_loc, lse=l_loc)
+    scores = msa.msa_route_scores(x["q_r"], x["kbar_r"], x["knorm"], cpd)
+    ids, _ = msa.msa_topk_docs(scores, topk)
+    k_sel, v_sel = msa.msa_gather_kv(x["kbar"], x["vbar"], ids, cpd)
+    o_mem, l_mem = msa.msa_sparse_attn(x["q"], None, None, k_sel, v_sel)
+    cur.wait_stream(side)
+    out, lse = msa.msa_attn_merge(o_loc, l_loc, o_mem, l_mem)
+    torch.cuda.synchronize()
+    ro, rlse = sparse_attention(to_f64(x["q"]), to_f64(k_sel), to_f64(v_sel), to_f64(x["k_loc"]),
+                                to_f64(x["v_loc"]), scale=1.0 / math.sqrt(cfg.dim))
+    rel = row_rel_l2(to_f64(out), ro)
+    lerr = np.abs(to_f64(lse) - rlse)
+    print(f"  overlapped attention: max row rel-L2 {rel.max():.2e} over {rel.size} rows, max |lse err| {lerr.max():.2e}")
+    assert rel.shape == (32, 1, 32) and rel.max() <= ATTN_RTOL_BF16
+    assert lerr.max() <= 2e-3

@@ -88,3 +88,63 @@ def test_graph_replays_match_eager_steps():
     torch.cuda.synchronize()
     for a, b in zip(got, step.results()):
         assert torch.equal(a, b)
+
+
+class _OverlapStep(_Step):
+    """The same step with the attention in two parts, as the decode bench runs
+    it: the local rows' attention forked onto a second stream at the start,
+    the memory rows' attention after the gather, a log-sum-exp merge after the
+    join."""
+
+    def __init__(self, t):
+        super().__init__(t)
+        self.aux = torch.cuda.Stream()
+        self.o_loc, self.o_mem = torch.empty_like(self.out), torch.empty_like(self.out)
+        self.l_loc, self.l_mem = torch.empty_like(self.lse), torch.empty_like(self.lse)
+
+    def __call__(self):
+        t = self.t
+        cur = torch.cuda.current_stream()
+        self.aux.wait_stream(cur)
+        with torch.cuda.stream(self.aux):
+            msa.msa_sparse_attn(t["q"], None, None, t["k_loc"], t["v_loc"], out=self.o_loc, lse=self.l_loc)
+        msa.msa_route_scores(t["q_r"], t["kbar_r"], t["knorm"], t["cpd"], doc_scores=self.scores)
+        msa.msa_topk_docs(self.scores, t["topk"], topk_ids=self.ids, topk_scores=self.top)
+        msa.msa_gather_kv(t["kbar"], t["vbar"], self.ids, t["cpd"], k_sel=self.k_sel, v_sel=self.v_sel)
+        msa.msa_sparse_attn(t["q"], None, None, self.k_sel, self.v_sel, out=self.o_mem, lse=self.l_mem)
+        cur.wait_stream(self.aux)
+        msa.msa_attn_merge(self.o_loc, self.l_loc, self.o_mem, self.l_mem, out=self.out, lse=self.lse)
+
+
+def test_two_stream_graph_replays_match_eager_steps():
+    t = _inputs(8)
+    step = _OverlapStep(t)
+    step()
+    torch.cuda.synchronize()
+    want = step.results()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    other = _OverlapStep(_inputs(9))
+    for rep in range(4):
+        for x in (step.scores, step.out, step.lse, step.o_loc, step.o_mem):
+            x.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(step.results(), want):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager step"
+        other()
+        torch.cuda.synchronize()
+    # the overlapped step agrees with the one-call attention to the bf16 tolerance
+    plain = _Step(t)
+    plain()
+    torch.cuda.synchronize()
+    rel = ((step.out.float() - plain.out.float()).norm(dim=-1) / plain.out.float().norm(dim=-1)).max().item()
+    assert rel <= 2e-2, rel
+    assert (step.lse - plain.lse).abs().max().item() <= 2e-3

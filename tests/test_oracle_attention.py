@@ -18,7 +18,8 @@ import torch
 from scipy.special import softmax
 
 import msa_inputs as mi
-from oracle import (gather_kv, pool_chunks_stored, route_scores, sparse_attention, topk_docs)
+from oracle import (gather_kv, merge_attention, pool_chunks_stored, route_scores, sparse_attention,
+                    sparse_attention_rows, topk_docs)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -166,3 +167,82 @@ def test_all_documents_selected_equals_dense_sdpa():
         mask[tt, : m + l_len - t_len + tt + 1] = True
     ref = torch.nn.functional.scaled_dot_product_attention(qq, keys, vals, attn_mask=mask)
     np.testing.assert_allclose(o, ref.permute(0, 2, 1, 3).numpy(), atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# merge of two partial attentions over disjoint key sets
+# ---------------------------------------------------------------------------
+
+def _memory_only(q, ks, vs, scale):
+    """Attention of every query row over the memory rows alone (brute force per row)."""
+    b_, t_, hq, _ = q.shape
+    g = hq // ks.shape[2]
+    o = np.zeros_like(q)
+    lse = np.zeros((b_, hq, t_))
+    for b in range(b_):
+        for h in range(hq):
+            for t in range(t_):
+                o[b, t, h], lse[b, h, t] = sparse_attention_rows(q[b, t, h], ks[b, :, h // g], vs[b, :, h // g], scale)
+    return o, lse
+
+
+@pytest.mark.parametrize("t_len,l_len", [(3, 5), (1, 4)])
+def test_merge_of_disjoint_parts_equals_attention_over_their_union(t_len, l_len):
+    # memory rows and visible local rows are disjoint key sets; merging the
+    # attention over each must give the attention over all of them
+    rng = np.random.default_rng(40 + t_len)
+    q = rng.standard_normal((2, t_len, 4, 8))
+    ks, vs = rng.standard_normal((2, 5, 2, 8)), rng.standard_normal((2, 5, 2, 8))
+    kl, vl = rng.standard_normal((2, l_len, 2, 8)), rng.standard_normal((2, l_len, 2, 8))
+    o, lse = sparse_attention(q, ks, vs, kl, vl, scale=0.6)
+    empty = np.zeros((2, 0, 2, 8))
+    o_loc, lse_loc = sparse_attention(q, empty, empty, kl, vl, scale=0.6)
+    o_mem, lse_mem = _memory_only(q, ks, vs, 0.6)
+    mo, mlse = merge_attention(o_loc, lse_loc, o_mem, lse_mem)
+    np.testing.assert_allclose(mo, o, atol=1e-13)
+    np.testing.assert_allclose(mlse, lse, atol=1e-13)
+    # the merge is symmetric in its two parts
+    mo2, mlse2 = merge_attention(o_mem, lse_mem, o_loc, lse_loc)
+    np.testing.assert_allclose(mo2, o, atol=1e-13)
+    np.testing.assert_allclose(mlse2, lse, atol=1e-13)
+
+
+def test_merge_decode_memory_rows_passed_as_local_rows():
+    # one query token sees every local row, so the memory rows' attention is
+    # the attention over them passed as local rows of a call without memory
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((3, 1, 4, 8))
+    ks, vs = rng.standard_normal((3, 6, 2, 8)), rng.standard_normal((3, 6, 2, 8))
+    kl, vl = rng.standard_normal((3, 9, 2, 8)), rng.standard_normal((3, 9, 2, 8))
+    empty = np.zeros((3, 0, 2, 8))
+    o, lse = sparse_attention(q, ks, vs, kl, vl)
+    o_loc, lse_loc = sparse_attention(q, empty, empty, kl, vl)
+    o_mem, lse_mem = sparse_attention(q, empty, empty, ks, vs)
+    mo, mlse = merge_attention(o_loc, lse_loc, o_mem, lse_mem)
+    np.testing.assert_allclose(mo, o, atol=1e-13)
+    np.testing.assert_allclose(mlse, lse, atol=1e-13)
+
+
+def test_merge_closed_forms():
+    rng = np.random.default_rng(3)
+    o_a, o_b = rng.standard_normal((2, 3, 4, 8)), rng.standard_normal((2, 3, 4, 8))
+    lse_a = rng.standard_normal((2, 4, 3))
+    # equal normalisers: the mean of the two outputs, log-sum-exp up by log 2
+    mo, mlse = merge_attention(o_a, lse_a, o_b, lse_a)
+    np.testing.assert_allclose(mo, (o_a + o_b) / 2, atol=1e-14)
+    np.testing.assert_allclose(mlse, lse_a + math.log(2.0), atol=1e-14)
+    # an empty part (lse = -inf) contributes nothing
+    none = np.full((2, 4, 3), -np.inf)
+    mo, mlse = merge_attention(o_a, lse_a, o_b, none)
+    np.testing.assert_array_equal(mo, o_a)
+    np.testing.assert_array_equal(mlse, lse_a)
+    # both empty: zero output, -inf
+    mo, mlse = merge_attention(o_a, none, o_b, none)
+    np.testing.assert_array_equal(mo, np.zeros_like(o_a))
+    assert np.all(np.isneginf(mlse))
+    # one (b, h, t) weighted by hand: lse_a = log 1, lse_b = log 3 -> weights 1/4, 3/4
+    la, lb = np.zeros((1, 1, 1)), np.full((1, 1, 1), math.log(3.0))
+    xa, xb = np.array([[[[4.0, 0.0]]]]), np.array([[[[0.0, 8.0]]]])
+    mo, mlse = merge_attention(xa, la, xb, lb)
+    np.testing.assert_allclose(mo, [[[[1.0, 6.0]]]], atol=1e-15)
+    np.testing.assert_allclose(mlse, [[[math.log(4.0)]]], atol=1e-15)
