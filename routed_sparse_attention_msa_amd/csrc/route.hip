@@ -684,6 +684,32 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
     const int c = tid + kTiledThreads * i;
     voff[i] = (uint32_t)(c >> 3) * row_bytes + (c & 7) * 16;
   }
+  // LDS byte addresses.  The key buffers start at 64 KiB, past the reach of a
+  // DS instruction's 16-bit offset, so each lane's addresses carry their
+  // buffer's base: every access is then (lane address) + (constant offset),
+  // with no address arithmetic in the loop.  A 32-row block moves an
+  // address by 32 * 128 B and leaves its swizzle ((row / 2) % 8) unchanged;
+  // so does a staging piece (64 rows).
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  const uint32_t q_lds = (uint32_t)(uintptr_t)(lds_u8*)(&sm.q[0][0]);
+  const uint32_t k_lds = (uint32_t)(uintptr_t)(lds_u8*)(&sm.k[0][0]);
+  // (Each address is passed through an empty asm: the compiler otherwise
+  // splits it into shared parts and adds them back before every access.)
+  uint32_t q_rd[4], k_rd[4];   // operand reads of k step s: row block 0, buffer 0
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    q_rd[s] = q_lds + (uint32_t)swz(wm * 128 + cl, 4 * hf + s);
+    k_rd[s] = k_lds + (uint32_t)swz(wn * 64 + cl, 4 * hf + s);
+    asm("" : "+v"(q_rd[s]));
+    asm("" : "+v"(k_rd[s]));
+  }
+  uint32_t q_st = q_lds + (uint32_t)swz(tid >> 3, tid & 7);   // staging piece 0, buffer 0
+  uint32_t k_st = k_lds + (uint32_t)swz(tid >> 3, tid & 7);
+  asm("" : "+v"(q_st));
+  asm("" : "+v"(k_st));
+  constexpr uint32_t kBufBytes = kTB * kStageK * 2;
+  static_assert(kTB * kStageK * 2 == kNB * kStageK * 2, "q and k buffers have one size");
+  static_assert(kBufBytes + 3 * 64 * 128 < 65536 && kBufBytes + 3 * 32 * 128 < 65536, "offsets must fit 16 bits");
 
   // first tile of this workgroup: its tables, stage 0 in buffer 0, stage 1 in registers
   unsigned v = blockIdx.x;
@@ -708,11 +734,10 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
     pq[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ld_q, voff[i], soff, 0));
     pk[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ld_k, voff[i], soff, 0));
   };
-  auto lstore1 = [&](int buf, int i) {
-    const int c = tid + kTiledThreads * i;
-    const int r = c >> 3, seg = c & 7;
-    *reinterpret_cast<u32x4*>(&sm.q[buf][swz(r, seg)]) = pq[i];
-    *reinterpret_cast<u32x4*>(&sm.k[buf][swz(r, seg)]) = pk[i];
+  auto lstore1 = [&](int buf, int i) {   // piece i: rows 64 i + tid / 8
+    const uint32_t off = (uint32_t)buf * kBufBytes + (uint32_t)i * 64 * 128;
+    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>((uintptr_t)(q_st + off)) = pq[i];
+    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>((uintptr_t)(k_st + off)) = pk[i];
   };
   load_tables(ty * kTB, tx * kNB);
   store_tables();
@@ -728,16 +753,24 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
   // chain to head hn (or, with hn == heads, apply the final scale); the four
   // factor reads of a row block are issued together, so their LDS latencies
   // overlap.
+  // (the tables sit past 128 KiB: the lane's address of head 0, plus the head's row)
+  uint32_t rq_lane = (uint32_t)(uintptr_t)(lds_u8*)(&sm.rq[0][wm * 128 + 4 * hf]);
+  uint32_t rk_lane = (uint32_t)(uintptr_t)(lds_u8*)(&sm.rk[0][wn * 64 + cl]);
+  asm("" : "+v"(rq_lane));
+  asm("" : "+v"(rk_lane));
   auto rescale = [&](int hn) {
+    const uint32_t rqa = rq_lane + (uint32_t)hn * kTB * 4, rka = rk_lane + (uint32_t)hn * kNB * 4;
     float ck[2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) ck[b] = sm.rk[hn][wn * 64 + b * 32 + cl];
+    for (int b = 0; b < 2; ++b)
+      ck[b] = *reinterpret_cast<__attribute__((address_space(3))) const float*>((uintptr_t)(rka + (uint32_t)b * 32 * 4));
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       f32x4 rq4[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        rq4[q] = *reinterpret_cast<const f32x4*>(&sm.rq[hn][wm * 128 + a * 32 + 8 * q + 4 * hf]);
+        rq4[q] = *reinterpret_cast<__attribute__((address_space(3))) const f32x4*>(
+            (uintptr_t)(rqa + (uint32_t)(a * 32 + 8 * q) * 4));
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -753,22 +786,16 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
   // the matrix core is busy instead of after the stage, and each load has a
   // whole stage to land before its store.
   auto stage_mfma = [&](int buf, int nbuf, int nstage) {
-    const uint8_t* qs = sm.q[buf];
-    const uint8_t* ks = sm.k[buf];
+    typedef __attribute__((address_space(3))) const bf16x8 lds_frag;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int seg = 4 * hf + s;
       bf16x8 af[4], bfr[2];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int r = wm * 128 + a * 32 + cl;
-        af[a] = *reinterpret_cast<const bf16x8*>(qs + swz(r, seg));
-      }
+      for (int a = 0; a < 4; ++a)
+        af[a] = *reinterpret_cast<lds_frag*>((uintptr_t)(q_rd[s] + (uint32_t)buf * kBufBytes + (uint32_t)a * 32 * 128));
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int r = wn * 64 + b * 32 + cl;
-        bfr[b] = *reinterpret_cast<const bf16x8*>(ks + swz(r, seg));
-      }
+      for (int b = 0; b < 2; ++b)
+        bfr[b] = *reinterpret_cast<lds_frag*>((uintptr_t)(k_rd[s] + (uint32_t)buf * kBufBytes + (uint32_t)b * 32 * 128));
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
