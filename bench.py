@@ -162,19 +162,6 @@ def work_attn(cfg):
     return {"bound": "mfma" if flops / b > ridge else "hbm", "bytes": b, "flops": flops}
 
 
-def work_merge(cfg):
-    # two partial outputs and their log-sum-exps in, the merged output and log-sum-exp out
-    b_, t_ = cfg.batch, cfg.q_len
-    b = 3 * b_ * t_ * cfg.heads_q * cfg.dim * 2 + 3 * b_ * cfg.heads_q * t_ * 4
-    return {"bound": "hbm", "bytes": b, "flops": 0}
-
-
-# stages whose one call launches the same kernel more than once (the decode
-# attention: the local rows, then the memory rows); their per-launch figures
-# are the call's time and work over that count
-LAUNCHES_PER_CALL = {("decode", "attn"): 2}
-
-
 def host_threads():
     """Host threads the oracle runs on: `cores` is the BLAS thread count (its
     matrix products use them; its element-wise NumPy work runs on one), beside
@@ -228,11 +215,8 @@ STAGE_KERNELS = {
     "prefill": {"pool": ("pool_kernel", "pool.hip"), "route": ("route_", "route.hip"),
                 "topk": ("topk", "topk.hip"), "gather": ("gather", "gather.hip"),
                 "attn": ("attn_prefill", "attn_prefill.hip")},
-    # (decode: the attention stage launches the decode kernel twice, local rows then memory rows; its
-    #  entry is twice the mean over the kernel's launches, the stage's bytes per call)
     "decode": {"route": ("route_", "route.hip"), "topk": ("topk", "topk.hip"),
-               "gather": ("gather", "gather.hip"), "attn": ("attn_decode", "attn_decode.hip", 2, "mean"),
-               "merge": ("attn_merge", "attn_merge.hip")},
+               "gather": ("gather", "gather.hip"), "attn": ("attn_decode", "attn_decode.hip")},
     # (the rounds' routing is one launch over all rounds' queries; each round has its own top-k launch)
     "interleave": {"rounds": ("route_|topk", "route.hip|topk.hip", {"route_": 1, "topk": INTERLEAVE_ROUNDS}),
                    "gather": ("gather", "gather.hip"),
@@ -283,14 +267,6 @@ def _per_kernel_median(rows):
     return {k: sorted(v)[len(v) // 2] for k, v in by.items()}
 
 
-def _per_kernel_mean(rows):
-    """kernel name -> mean of the counter over its dispatches (KiB)."""
-    by = {}
-    for r in rows:
-        by.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-    return {k: sum(v) / len(v) for k, v in by.items()}
-
-
 def _short_kernel(name):
     import re
     m = re.search(r"msa::\(anonymous namespace\)::([a-z_0-9]+(?:<[^>(]*>)?)", name)
@@ -326,17 +302,14 @@ def summarize_traffic(d):
            "counter KiB into bytes.", "",
            "| workload | stage | kernels | read MB | written MB | total MB per launch |", "|---|---|---|---|---|---|"]
     for wl, stages in STAGE_KERNELS.items():
-        rows_f = _counter_rows(os.path.join(d, f"{wl}_fetch"))
-        rows_w = _counter_rows(os.path.join(d, f"{wl}_write"))
-        if not rows_f or not rows_w:
+        fm = _per_kernel_median(_counter_rows(os.path.join(d, f"{wl}_fetch")))
+        wm = _per_kernel_median(_counter_rows(os.path.join(d, f"{wl}_write")))
+        if not fm or not wm:
             continue
         out[wl] = {}
         for stage, spec in stages.items():
             pat, src = spec[0], spec[1]
             per_call = spec[2] if len(spec) > 2 else 1          # launches of each kernel per stage call
-            # median over a kernel's launches, or their mean where one call's launches differ in size
-            stat = _per_kernel_mean if len(spec) > 3 and spec[3] == "mean" else _per_kernel_median
-            fm, wm = stat(rows_f), stat(rows_w)
             names = sorted(k for k in fm if "msa::" in k and any(p in k for p in pat.split("|")))
             if not names:
                 continue
@@ -490,16 +463,6 @@ class Step:
         self.ws_attn = u8(msa.msa_sparse_attn_workspace(cfg.batch, cfg.q_len, cfg.heads_q, cfg.heads_kv,
                                                         cfg.dim, rounds * cfg.mem_len, cfg.loc_len,
                                                         torch.bfloat16))
-        if workload == "decode":
-            # the attention in two parts: the local rows (no routing needed) and
-            # the selected memory rows, merged by their log-sum-exp
-            self.o_loc, self.o_mem = torch.empty_like(t["q"]), torch.empty_like(t["q"])
-            self.l_loc, self.l_mem = torch.empty_like(self.lse), torch.empty_like(self.lse)
-            self.ws_loc = u8(msa.msa_sparse_attn_workspace(cfg.batch, cfg.q_len, cfg.heads_q, cfg.heads_kv,
-                                                           cfg.dim, 0, cfg.loc_len, torch.bfloat16))
-            self.ws_mem = u8(msa.msa_sparse_attn_workspace(cfg.batch, cfg.q_len, cfg.heads_q, cfg.heads_kv,
-                                                           cfg.dim, 0, cfg.mem_len, torch.bfloat16))
-            self.aux = torch.cuda.Stream(device=dev)
         if workload == "interleave":
             self.ws_rounds = u8(msa.msa_route_rounds_workspace(rounds, cfg.batch, cfg.q_len, cfg.heads_kv,
                                                                cfg.dim, cfg.n_doc, cpd, cfg.topk,
@@ -526,59 +489,13 @@ class Step:
                                                        doc_scores=self.scores, ws=self.ws_route)),
                 ("topk", lambda: msa.msa_topk_docs(self.scores, cfg.topk, topk_ids=self.ids,
                                                    topk_scores=self.top, ws=self.ws_topk))]
-        seq += [("gather", lambda: msa.msa_gather_kv(self.kbar, self.vbar, self.ids, cfg.chunks_per_doc,
-                                                     k_sel=self.k_sel, v_sel=self.v_sel))]
-        if self.workload == "decode":
-            def attn():
-                self._attn_local()
-                self._attn_mem()
-            seq += [("attn", attn), ("merge", self._merge)]
-        else:
-            seq += [("attn", lambda: msa.msa_sparse_attn(t["q"], self.k_sel, self.v_sel, t["k_loc"], t["v_loc"],
-                                                         out=self.out, lse=self.lse, ws=self.ws_attn))]
+        seq += [
+            ("gather", lambda: msa.msa_gather_kv(self.kbar, self.vbar, self.ids, cfg.chunks_per_doc,
+                                                 k_sel=self.k_sel, v_sel=self.v_sel)),
+            ("attn", lambda: msa.msa_sparse_attn(t["q"], self.k_sel, self.v_sel, t["k_loc"], t["v_loc"],
+                                                 out=self.out, lse=self.lse, ws=self.ws_attn)),
+        ]
         return seq
-
-    # decode: the local rows' attention does not depend on routing; the memory
-    # rows (k_sel/v_sel) go in as the local rows of a call without memory,
-    # which the one query token sees in full
-    def _attn_local(self):
-        t = self.t
-        self.msa.msa_sparse_attn(t["q"], None, None, t["k_loc"], t["v_loc"], out=self.o_loc, lse=self.l_loc,
-                                 ws=self.ws_loc)
-
-    def _attn_mem(self):
-        self.msa.msa_sparse_attn(self.t["q"], None, None, self.k_sel, self.v_sel, out=self.o_mem, lse=self.l_mem,
-                                 ws=self.ws_mem)
-
-    def _merge(self):
-        self.msa.msa_attn_merge(self.o_loc, self.l_loc, self.o_mem, self.l_mem, out=self.out, lse=self.lse)
-
-    def body(self):
-        """One whole step, as the graph captures it.  Decode forks the local
-        rows' attention onto a second stream once the routing scan is done,
-        beside top-k -> gather -> the memory rows' attention, and joins it
-        before the merge; the other workloads run their calls in order.  (The
-        attention holds one workgroup per CU at 384 registers a wave for its
-        whole run, which leaves no room for the routing scan's workgroups: a
-        scan started beside it would wait for it.  Top-k and gather fit.)"""
-        torch = self.torch
-        if self.workload != "decode":
-            for _, fn in self.calls():
-                fn()
-            return
-        cur = torch.cuda.current_stream()
-        for stage, fn in self.calls():
-            if stage == "attn":
-                self._attn_mem()
-            elif stage == "merge":
-                cur.wait_stream(self.aux)
-                fn()
-            else:
-                fn()
-            if stage == "route":
-                self.aux.wait_stream(cur)
-                with torch.cuda.stream(self.aux):
-                    self._attn_local()
 
     def pool_calls(self):
         """The offline stage (S1): pool K, V and K_r (+ norms) into the bank."""
@@ -1367,24 +1284,21 @@ def graph_replay_ms(step, steps, warmup=2):
     makes no allocation and no host synchronisation, and the library records
     no memset, so the graph holds only the step's kernels.  Replays remove
     the per-launch host cost (the Python binding and the launches) that the
-    eager loop pays between short kernels.  A step with a `body()` (decode:
-    two streams) is captured through it, any other as its calls in order."""
+    eager loop pays between short kernels."""
     import torch
-
-    def sequential():
-        for _, fn in step.calls():
-            fn()
-    body = getattr(step, "body", None) or sequential
+    seq = step.calls()
     try:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            body()
+            for _, fn in seq:
+                fn()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            body()
+            for _, fn in seq:
+                fn()
     except Exception as e:  # pragma: no cover - reported, eager timing stands
         print(f"[bench] graph capture failed ({e}); eager timing only", file=sys.stderr, flush=True)
         return None
@@ -1651,7 +1565,7 @@ def main():
 
     mem_cfg = dataclasses.replace(cfg, topk=rounds * cfg.topk)      # the memory all rounds gathered
     works = {"pool": None, "route": work_route(cfg), "topk": work_topk(cfg), "gather": work_gather(mem_cfg),
-             "attn": work_attn(mem_cfg), "rounds": work_rounds(cfg, rounds), "merge": work_merge(cfg)}
+             "attn": work_attn(mem_cfg), "rounds": work_rounds(cfg, rounds)}
     per = {}
     counts = {}
     for stage, a, b in marks:
@@ -1659,22 +1573,17 @@ def main():
         counts[stage] = counts.get(stage, 0) + 1
     stages = {}
     for stage in per:
-        n_call = counts[stage]
-        per_call = LAUNCHES_PER_CALL.get((args.workload, stage), 1)
-        call_ms = per[stage] / n_call
+        n_launch = counts[stage]
+        avg = per[stage] / n_launch
         w = works[stage] if stage != "pool" else work_pool(cfg, with_norm=False)
-        entry = roofline_entry(w, call_ms)        # (work per call over time per call = per launch over per launch)
-        entry.update({"avg_launch_ms": call_ms / per_call, "launches_per_step": per_call * n_call // args.steps,
+        entry = roofline_entry(w, avg)
+        entry.update({"avg_launch_ms": avg, "launches_per_step": n_launch // args.steps,
                       "ms_per_step": per[stage] / args.steps})
-        if per_call > 1:
-            entry["launches_per_call"] = per_call
         stages[stage] = entry
     dom = max(stages, key=lambda s: stages[s]["ms_per_step"])
     roof = {k: stages[dom][k] for k in ("bound", "achieved", "peak", "unit", "frac")}
     roof["kernel"] = dom
     roof["avg_launch_ms"] = stages[dom]["avg_launch_ms"]
-    if "launches_per_call" in stages[dom]:
-        roof["launches_per_call"] = stages[dom]["launches_per_call"]
     roof["traffic"] = measured_traffic(args.workload, dom)
 
     tokens = cfg.batch * cfg.q_len
@@ -1720,8 +1629,7 @@ def main():
                    "mem_len": rounds * cfg.mem_len,
                    "step": {"prefill": "route -> top-k -> gather -> attention (the bank pooled offline, "
                                        "timed apart: offline_pool)",
-                            "decode": "[second stream: attention over the local rows] beside route -> top-k -> "
-                                      "gather -> attention over the memory rows; log-sum-exp merge",
+                            "decode": "route -> top-k -> gather -> split-KV attention",
                             "interleave": f"(route -> top-k excluding earlier picks) x{rounds} -> gather -> "
                                           "attention"}[args.workload]},
         "roofline": roof,
