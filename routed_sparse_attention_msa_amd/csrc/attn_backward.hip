@@ -482,12 +482,17 @@ __global__ __launch_bounds__(NWK * 64) void attn_bwd_dkdv_kernel(
         // accumulator, or a select the compiler turned back into control
         // flow) made a branch per element, around which every dK/dV
         // accumulator was copied out of its registers and back on every tile.
-        const unsigned masked = __all(key_ok && (mem || kappa_row <= shift + tq0)) ? 0u : 1u;   // uniform
-        const unsigned key_bad = key_ok ? 0u : 1u, local = mem ? 0u : 1u;
+        // Element i holds query row 4 hf + c_i of the tile (c_i = 8 (i / 4) + i % 4,
+        // 0 .. 27) and is hidden exactly when c_i < u, with u per lane and item:
+        // above every c_i without a key, below every c_i for a memory row, and
+        // for a local row the first row that sees it less 4 hf (row r sees it
+        // iff kappa_row <= shift + tq0 + r), clamped to [-1, 32].  One
+        // subtract, shift and bit insert per element.
+        const int u = !key_ok ? 32 : (mem ? -1 : min(32, max(-1, kappa_row - shift - tq0 - 4 * hf)));
         auto arg = [&](int i) {
           const float x = fmaf(s[i], scale_log2, -l2[i]);
-          const unsigned late = kappa_row > shift + tq0 + acc_row(i, hf) ? 1u : 0u;
-          const unsigned m = 0u - (masked & (key_bad | (local & late)));        // all ones when hidden
+          const int c = 8 * (i >> 2) + (i & 3);
+          const unsigned m = (unsigned)((c - u) >> 31);                        // all ones when hidden
           return __uint_as_float((__float_as_uint(x) & ~m) | (0xFF800000u & m));
         };
         bf16x8 pf[2], dsf[2];
