@@ -785,24 +785,31 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
   // stage nstage, one piece per k step, so the stores and loads issue while
   // the matrix core is busy instead of after the stage, and each load has a
   // whole stage to land before its store.
+  // The operand reads run one k step ahead (two register sets): step s + 1's
+  // fragments are requested before step s's MFMAs issue.
   auto stage_mfma = [&](int buf, int nbuf, int nstage) {
     typedef __attribute__((address_space(3))) const bf16x8 lds_frag;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 af[4], bfr[2];
+    bf16x8 af[2][4], bfr[2][2];
+    auto read = [&](int s) {
 #pragma unroll
       for (int a = 0; a < 4; ++a)
-        af[a] = *reinterpret_cast<lds_frag*>((uintptr_t)(q_rd[s] + (uint32_t)buf * kBufBytes + (uint32_t)a * 32 * 128));
+        af[s & 1][a] = *reinterpret_cast<lds_frag*>((uintptr_t)(q_rd[s] + (uint32_t)buf * kBufBytes + (uint32_t)a * 32 * 128));
 #pragma unroll
       for (int b = 0; b < 2; ++b)
-        bfr[b] = *reinterpret_cast<lds_frag*>((uintptr_t)(k_rd[s] + (uint32_t)buf * kBufBytes + (uint32_t)b * 32 * 128));
+        bfr[s & 1][b] = *reinterpret_cast<lds_frag*>((uintptr_t)(k_rd[s] + (uint32_t)buf * kBufBytes + (uint32_t)b * 32 * 128));
+    };
+    read(0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);    // step 0's reads
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s < 3) read(s + 1);
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = mfma32(af[a], bfr[b], acc[a][b]);
+        for (int b = 0; b < 2; ++b) acc[a][b] = mfma32(af[s & 1][a], bfr[s & 1][b], acc[a][b]);
       lstore1(nbuf, s);
       gload1(nstage, s);
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // LDS reads of this step
+      if (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // LDS reads of the next step
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);  // LDS writes
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
