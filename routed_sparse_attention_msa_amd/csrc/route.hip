@@ -750,14 +750,14 @@ __global__ __launch_bounds__(kTiledThreads) void route_tiled_kernel(
   __syncthreads();
 
   f32x16 acc[4][2];
-  // chain to head hn (or, with hn == heads, apply the final scale); the four
-  // factor reads of a row block are issued together, so their LDS latencies
-  // overlap.
   // (the tables sit past 128 KiB: the lane's address of head 0, plus the head's row)
   uint32_t rq_lane = (uint32_t)(uintptr_t)(lds_u8*)(&sm.rq[0][wm * 128 + 4 * hf]);
   uint32_t rk_lane = (uint32_t)(uintptr_t)(lds_u8*)(&sm.rk[0][wn * 64 + cl]);
   asm("" : "+v"(rq_lane));
   asm("" : "+v"(rk_lane));
+  // chain to head hn (or, with hn == heads, apply the final scale); the four
+  // factor reads of a row block are issued together, so their LDS latencies
+  // overlap.
   auto rescale = [&](int hn) {
     const uint32_t rqa = rq_lane + (uint32_t)hn * kTB * 4, rka = rk_lane + (uint32_t)hn * kNB * 4;
     float ck[2];
