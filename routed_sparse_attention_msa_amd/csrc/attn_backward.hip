@@ -486,8 +486,8 @@ __global__ __launch_bounds__(NWK * 64) void attn_bwd_dkdv_kernel(
         // 0 .. 27) and is hidden exactly when c_i < u, with u per lane and item:
         // above every c_i without a key, below every c_i for a memory row, and
         // for a local row the first row that sees it less 4 hf (row r sees it
-        // iff kappa_row <= shift + tq0 + r), clamped to [-1, 32].  One
-        // subtract, shift and bit insert per element.
+        // iff kappa_row <= shift + tq0 + r), clamped to [-1, 32].  The compiler
+        // turns the sign mask into one compare and one select per element.
         const int u = !key_ok ? 32 : (mem ? -1 : min(32, max(-1, kappa_row - shift - tq0 - 4 * hf)));
         auto arg = [&](int i) {
           const float x = fmaf(s[i], scale_log2, -l2[i]);

@@ -320,7 +320,8 @@ __global__ __launch_bounds__(kThreads) void topk_small_kernel(
     a[i] = ok ? make_key(scores[(size_t)b * n + idx], (uint32_t)idx) : 0;
   }
   if (k >= 12 && k <= 16) {
-    // Threshold pass (for smaller k the extraction below, k wave maxima, is the quicker).  The 16 largest lane maxima of the row are 16 distinct
+    // Threshold pass (for smaller k the extraction below, k wave maxima, is
+    // the quicker).  The 16 largest lane maxima of the row are 16 distinct
     // keys, so the 16th largest lane maximum T is at most the row's 16th
     // largest key: the keys >= T hold the top k.  Each wave sorts its lanes'
     // maxima, the waves' 16 largest (64 values) are sorted again by every
