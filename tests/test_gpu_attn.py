@@ -66,6 +66,9 @@ def _check(q, ks, vs, kl, vl, rtol, lse_atol):
     (1, 1, 8, 1, 128, 64, 5000, torch.bfloat16),       # one pair: many runs of splits, combined
     (1, 96, 8, 2, 128, 64, 160, torch.bfloat16),       # 3 token blocks: a block pair and a middle block alone
     (1, 80, 16, 2, 128, 40, 100, torch.bfloat16),      # group of 8 heads (two head sub-groups), partial tiles
+    (2, 8, 32, 8, 128, 64, 300, torch.bfloat16),       # decode at its widest: 8 tokens x 4 heads = 32 columns
+    (1, 9, 32, 8, 128, 32, 300, torch.bfloat16),       # one token more: the prefill kernel, one ragged block
+    (4, 1, 32, 8, 128, 0, 500, torch.bfloat16),        # decode without memory rows (the local part alone)
 ])
 def test_attn_parity(batch, q_len, hq, hkv, dim, mem, loc, dtype):
     case(f"attn B={batch} T={q_len} Hq={hq} Hkv={hkv} d={dim} M={mem} L={loc} {dtype}")
